@@ -1,0 +1,95 @@
+"""Masked-token readout of a masked diffusion LLM on MI355X (gfx950).
+
+One step gathers the hidden states of still-masked positions, projects them
+through the LM head with a bf16 MFMA GEMM whose epilogue streams the
+vocabulary (running max / argmax / sum of exponentials, so no L x V logits
+tensor exists), and commits the k most confident positions.  The work runs
+in hand-written HIP kernels behind the C ABI in include/dllm_readout.h;
+this package is its thin Python binding.  PyTorch only provides device
+memory and streams.
+"""
+from __future__ import annotations
+
+from ._abi import (  # noqa: F401
+    DLLM_ERR_HIP,
+    DLLM_ERR_INVALID_ARG,
+    DLLM_ERR_UNSUPPORTED,
+    DLLM_ERR_WORKSPACE,
+    DLLM_K_MAX_LIMIT,
+    DLLM_OK,
+    EXPORTED,
+    LIB_PATH,
+    DllmError,
+    dllm_masked_readout_create,
+    dllm_masked_readout_destroy,
+    dllm_masked_readout_set_slices,
+    dllm_masked_readout_step,
+    dllm_masked_readout_workspace_bytes,
+    dllm_status_string,
+    load,
+)
+
+
+class MaskedReadout:
+    """A handle plus its torch-allocated workspace.
+
+    ``W_lm`` is a [V, d] torch.bfloat16 (or int16 bit-pattern) CUDA tensor
+    that must stay alive as long as this object."""
+
+    def __init__(self, W_lm, L_max: int, k_max: int, stream=None):
+        import torch
+        if not W_lm.is_cuda:
+            raise ValueError("W_lm must be a device tensor")
+        V, d = W_lm.shape
+        self.V, self.d, self.L_max, self.k_max = int(V), int(d), int(L_max), int(k_max)
+        nbytes = dllm_masked_readout_workspace_bytes(L_max, d, V, k_max)
+        if nbytes == 0:
+            raise DllmError(DLLM_ERR_INVALID_ARG, "dllm_masked_readout_workspace_bytes")
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=W_lm.device)
+        self.W_lm = W_lm
+        self.stream = stream if stream is not None else torch.cuda.current_stream(W_lm.device)
+        st, h = dllm_masked_readout_create(W_lm, self.V, self.d, L_max, k_max, self.workspace, nbytes,
+                                           self.stream)
+        if st != DLLM_OK:
+            raise DllmError(st, "dllm_masked_readout_create")
+        self.handle = h
+
+    def set_slices(self, slices: int) -> None:
+        st = dllm_masked_readout_set_slices(self.handle, slices)
+        if st != DLLM_OK:
+            raise DllmError(st, "dllm_masked_readout_set_slices")
+
+    def outputs(self):
+        """Freshly allocated output buffers for step()."""
+        import torch
+        dev = self.W_lm.device
+        i32 = dict(dtype=torch.int32, device=dev)
+        f32 = dict(dtype=torch.float32, device=dev)
+        K, L = max(self.k_max, 1), self.L_max
+        return dict(n_out=torch.zeros(1, **i32), m_out=torch.zeros(1, **i32),
+                    sel_idx=torch.full((K,), -1, **i32), sel_tok=torch.full((K,), -1, **i32),
+                    sel_conf=torch.zeros(K, **f32), row_idx=torch.full((L,), -1, **i32),
+                    row_tok=torch.full((L,), -1, **i32), row_conf=torch.zeros(L, **f32),
+                    row_lse=torch.zeros(L, **f32))
+
+    def step(self, hidden, mask, tokens, k: int, win_lo: int = 0, win_hi: int | None = None,
+             block: int = 0, out: dict | None = None) -> None:
+        """Queue one readout step on the handle's stream (asynchronous)."""
+        L = int(hidden.shape[0])
+        if win_hi is None:
+            win_hi = L
+        st = dllm_masked_readout_step(self.handle, hidden, L, mask, tokens, int(k), int(win_lo), int(win_hi),
+                                      int(block), out)
+        if st != DLLM_OK:
+            raise DllmError(st, "dllm_masked_readout_step")
+
+    def close(self) -> None:
+        if getattr(self, "handle", None):
+            dllm_masked_readout_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,131 @@
+"""ctypes binding of libdllm_readout.so (argument marshalling only).
+
+The functions carry the C names and C argument order; device buffers may be
+given as torch tensors (their data pointers are passed) or plain integers.
+Every step of the readout runs in the library's HIP kernels; there is no
+Python or CPU fallback, and loading fails loudly when the library is absent.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdllm_readout.so")
+
+DLLM_OK = 0
+DLLM_ERR_INVALID_ARG = 1
+DLLM_ERR_UNSUPPORTED = 2
+DLLM_ERR_WORKSPACE = 3
+DLLM_ERR_HIP = 4
+DLLM_K_MAX_LIMIT = 4096
+
+EXPORTED = (
+    "dllm_masked_readout_workspace_bytes",
+    "dllm_masked_readout_create",
+    "dllm_masked_readout_step",
+    "dllm_masked_readout_destroy",
+    "dllm_status_string",
+    "dllm_masked_readout_set_slices",
+)
+
+
+class dllm_step_out(C.Structure):
+    _fields_ = [
+        ("n_out", C.c_void_p),
+        ("m_out", C.c_void_p),
+        ("sel_idx", C.c_void_p),
+        ("sel_tok", C.c_void_p),
+        ("sel_conf", C.c_void_p),
+        ("row_idx", C.c_void_p),
+        ("row_tok", C.c_void_p),
+        ("row_conf", C.c_void_p),
+        ("row_lse", C.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m masked_token_logits_amd.build`")
+    lib = C.CDLL(path)
+    lib.dllm_masked_readout_workspace_bytes.restype = C.c_size_t
+    lib.dllm_masked_readout_workspace_bytes.argtypes = [C.c_int64, C.c_int64, C.c_int64, C.c_int32]
+    lib.dllm_masked_readout_create.restype = C.c_int
+    lib.dllm_masked_readout_create.argtypes = [C.POINTER(C.c_void_p), C.c_void_p, C.c_int64, C.c_int64,
+                                               C.c_int64, C.c_int32, C.c_void_p, C.c_size_t, C.c_void_p]
+    lib.dllm_masked_readout_step.restype = C.c_int
+    lib.dllm_masked_readout_step.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p,
+                                             C.c_int32, C.c_int64, C.c_int64, C.c_int64,
+                                             C.POINTER(dllm_step_out)]
+    lib.dllm_masked_readout_destroy.restype = C.c_int
+    lib.dllm_masked_readout_destroy.argtypes = [C.c_void_p]
+    lib.dllm_status_string.restype = C.c_char_p
+    lib.dllm_status_string.argtypes = [C.c_int]
+    lib.dllm_masked_readout_set_slices.restype = C.c_int
+    lib.dllm_masked_readout_set_slices.argtypes = [C.c_void_p, C.c_int32]
+    _lib = lib
+    return lib
+
+
+def _ptr(x) -> int | None:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+class DllmError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {dllm_status_string(status)} (status {status})")
+
+
+def dllm_status_string(status: int) -> str:
+    return load().dllm_status_string(int(status)).decode()
+
+
+def dllm_masked_readout_workspace_bytes(L_max: int, d: int, V: int, k_max: int) -> int:
+    return int(load().dllm_masked_readout_workspace_bytes(L_max, d, V, k_max))
+
+
+def dllm_masked_readout_create(W_lm, V: int, d: int, L_max: int, k_max: int, workspace,
+                               workspace_bytes: int, stream=None) -> tuple[int, int | None]:
+    """Returns (status, handle)."""
+    h = C.c_void_p()
+    st = load().dllm_masked_readout_create(C.byref(h), _ptr(W_lm), V, d, L_max, k_max, _ptr(workspace),
+                                           workspace_bytes, _stream(stream))
+    return st, h.value
+
+
+def dllm_masked_readout_step(handle, hidden, L: int, mask, tokens, k: int, win_lo: int, win_hi: int,
+                             block: int = 0, out: dict | None = None) -> int:
+    """``out`` maps dllm_step_out field names to device buffers (optional)."""
+    so = None
+    if out:
+        so = dllm_step_out(**{key: _ptr(v) for key, v in out.items()})
+    return load().dllm_masked_readout_step(handle, _ptr(hidden), L, _ptr(mask), _ptr(tokens), k, win_lo, win_hi,
+                                           block, C.byref(so) if so is not None else None)
+
+
+def dllm_masked_readout_destroy(handle) -> int:
+    return load().dllm_masked_readout_destroy(handle)
+
+
+def dllm_masked_readout_set_slices(handle, slices: int) -> int:
+    return load().dllm_masked_readout_set_slices(handle, slices)

@@ -1,0 +1,331 @@
+// Masked LM-head GEMM with a fused online vocabulary reduction.
+//
+// For each candidate row r (hidden state of a masked position, gathered
+// through the compacted index list) and each vocabulary entry v the logit is
+// z[r][v] = sum_k hidden[idx[r]][k] * W_lm[v][k]  (Mosaic, Abstract: the
+// LM-head logits computed only for masked positions).  The logits never
+// leave registers: every workgroup owns one tile of rows and one slice of
+// the vocabulary, walks the slice tile by tile in increasing vocabulary
+// order and keeps, per row, the running maximum m, the lowest index a that
+// attains it and s = sum exp(z - m) (the streaming form of max and
+// log-sum-exp), rescaling s whenever m grows.  One partial (m, a, s) per
+// (row, slice) is written; the merge kernel combines the slices.
+//
+// MI355X mapping
+//   * bf16 MFMA v_mfma_f32_32x32x16_bf16: A operand = 32 vocabulary rows of
+//     W_lm, B operand = 32 gathered hidden rows, fp32 accumulate.  With this
+//     orientation each lane's 16 accumulators of a 32x32 block are 16
+//     vocabulary entries of ONE row, so most of the reduction is in-lane.
+//   * W_lm and hidden tiles are staged through LDS (BK = 64 bf16 per stage,
+//     double buffered, global loads for stage s+1 in flight while stage s
+//     computes).  16-byte chunks are XOR-swizzled by row so that the
+//     ds_read_b128 fragment loads are bank-conflict free.
+//   * The gather is fused: each thread resolves its hidden-row pointers
+//     once through idx[] and streams them; no [M, d] copy exists.
+//   * Workgroup ids are remapped so that the workgroups resident on one XCD
+//     (ids congruent mod 8) own neighbouring (row tile, slice) pairs and
+//     share hidden tiles in that XCD's L2.
+//   * M is read on the device; row tiles past M exit at once, so the host
+//     never waits for the compaction result.
+#include "readout_internal.h"
+
+#include <math.h>
+
+namespace dllm {
+namespace {
+
+typedef short bf16x8 __attribute__((__vector_size__(8 * sizeof(short))));
+typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ int xcd_remap(int bid, int grid) {
+  constexpr int kXcd = 8;
+  const int per = grid / kXcd, rem = grid % kXcd;
+  const int x = bid % kXcd, loc = bid / kXcd;
+  return (x < rem) ? x * (per + 1) + loc : rem * (per + 1) + (x - rem) * per + loc;
+}
+
+// Merge two streaming states (m, a, s).  Ties on m keep the lower index.
+__device__ __forceinline__ void merge_state(float& m, int& a, float& s, float m2, int a2, float s2) {
+  const bool take2 = (m2 > m) || (m2 == m && a2 < a);
+  const float mn = fmaxf(m, m2);
+  const float e1 = (m == -INFINITY) ? 0.f : s * __builtin_amdgcn_exp2f((m - mn) * kLog2e);
+  const float e2 = (m2 == -INFINITY) ? 0.f : s2 * __builtin_amdgcn_exp2f((m2 - mn) * kLog2e);
+  a = take2 ? a2 : a;
+  m = mn;
+  s = e1 + e2;
+}
+
+template <int BM_, int BN_, int WM_, int WN_>
+struct Tile {
+  static constexpr int BM = BM_;             // candidate rows per workgroup
+  static constexpr int BN = BN_;             // vocabulary entries per tile
+  static constexpr int WM = WM_, WN = WN_;   // waves along rows / vocabulary
+  static constexpr int NT = WM * WN * 64;
+  static constexpr int WR = BM / WM;         // rows per wave
+  static constexpr int WV = BN / WN;         // vocabulary entries per wave
+  static constexpr int FR = WR / 32;         // 32x32 MFMA blocks along rows
+  static constexpr int FV = WV / 32;         // along vocabulary
+  static constexpr int CPR = kBK / 8;        // 16-byte chunks per LDS row
+  static constexpr int A_LD = BN * CPR / NT; // W chunks per thread per stage
+  static constexpr int B_LD = BM * CPR / NT; // hidden chunks per thread per stage
+  static_assert(BN * CPR % NT == 0 && BM * CPR % NT == 0, "tile / thread mismatch");
+  static_assert(WR % 32 == 0 && WV % 32 == 0, "wave tile must be whole MFMA blocks");
+  static_assert(CPR == 8, "swizzle assumes 8 chunks per row");
+};
+
+__device__ __forceinline__ int swz(int row, int chunk) { return row * kBK + ((chunk ^ (row & 7)) << 3); }
+
+template <class T>
+__global__ __launch_bounds__(T::NT) void k_gemm_online(const uint16_t* __restrict__ W,
+                                                       const uint16_t* __restrict__ H, int d, int V,
+                                                       const int32_t* __restrict__ idx,
+                                                       const int32_t* __restrict__ ctr, int slices,
+                                                       int n_vt, float* __restrict__ part_m,
+                                                       int32_t* __restrict__ part_a,
+                                                       float* __restrict__ part_s) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][T::BN * kBK];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][T::BM * kBK];
+
+  const int M = ctr[0];
+  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int rt = bid / slices;
+  const int slice = bid - rt * slices;
+  const int row0 = rt * T::BM;
+  if (row0 >= M) return;
+  const int vt_lo = (int)(((int64_t)slice * n_vt) / slices);
+  const int vt_hi = (int)(((int64_t)(slice + 1) * n_vt) / slices);
+  if (vt_lo >= vt_hi) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wr = wave / T::WN;  // wave row group
+  const int wv = wave % T::WN;  // wave vocabulary group
+  const int KT = (d + kBK - 1) / kBK;
+
+  // Per-thread load assignments (fixed for the workgroup's life).
+  int a_row[T::A_LD], a_ch[T::A_LD];
+#pragma unroll
+  for (int i = 0; i < T::A_LD; ++i) {
+    const int c = i * T::NT + tid;
+    a_row[i] = c / T::CPR;
+    a_ch[i] = c % T::CPR;
+  }
+  const uint16_t* b_ptr[T::B_LD];
+  int b_row[T::B_LD], b_ch[T::B_LD];
+#pragma unroll
+  for (int i = 0; i < T::B_LD; ++i) {
+    const int c = i * T::NT + tid;
+    b_row[i] = c / T::CPR;
+    b_ch[i] = c % T::CPR;
+    int r = row0 + b_row[i];
+    r = r < M ? r : M - 1;  // rows past M read a valid row; their results are dropped
+    b_ptr[i] = H + (size_t)idx[r] * (size_t)d;
+  }
+
+  bf16x8 ra[T::A_LD], rb[T::B_LD];
+  const bf16x8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+
+  auto gload = [&](int vt, int ks) {
+    const int k0 = ks * kBK;
+    const int v0 = vt * T::BN;
+#pragma unroll
+    for (int i = 0; i < T::A_LD; ++i) {
+      int v = v0 + a_row[i];
+      v = v < V ? v : V - 1;
+      const int k = k0 + a_ch[i] * 8;
+      ra[i] = (k < d) ? *reinterpret_cast<const bf16x8*>(W + (size_t)v * (size_t)d + k) : zero8;
+    }
+#pragma unroll
+    for (int i = 0; i < T::B_LD; ++i) {
+      const int k = k0 + b_ch[i] * 8;
+      rb[i] = (k < d) ? *reinterpret_cast<const bf16x8*>(b_ptr[i] + k) : zero8;
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < T::A_LD; ++i)
+      *reinterpret_cast<bf16x8*>(&sA[buf][swz(a_row[i], a_ch[i])]) = ra[i];
+#pragma unroll
+    for (int i = 0; i < T::B_LD; ++i)
+      *reinterpret_cast<bf16x8*>(&sB[buf][swz(b_row[i], b_ch[i])]) = rb[i];
+  };
+
+  f32x16 acc[T::FV][T::FR];
+  float run_m[T::FR], run_s[T::FR];
+  int run_a[T::FR];
+#pragma unroll
+  for (int fr = 0; fr < T::FR; ++fr) {
+    run_m[fr] = -INFINITY;
+    run_s[fr] = 0.f;
+    run_a[fr] = 0;
+  }
+#pragma unroll
+  for (int fv = 0; fv < T::FV; ++fv)
+#pragma unroll
+    for (int fr = 0; fr < T::FR; ++fr)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[fv][fr][e] = 0.f;
+
+  const int total = (vt_hi - vt_lo) * KT;
+  int vt = vt_lo, ks = 0;
+  gload(vt, ks);
+  lstore(0);
+  __syncthreads();
+
+  const int frag_row = lane & 31;
+  const int frag_half = lane >> 5;
+
+  for (int s = 0; s < total; ++s) {
+    const int buf = s & 1;
+    int nvt = vt, nks = ks + 1;
+    if (nks == KT) {
+      nks = 0;
+      ++nvt;
+    }
+    const bool has_next = (s + 1) < total;
+    if (has_next) gload(nvt, nks);
+
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+      const int ch = kk * 2 + frag_half;
+      bf16x8 fa[T::FV], fb[T::FR];
+#pragma unroll
+      for (int fv = 0; fv < T::FV; ++fv) {
+        const int r = wv * T::WV + fv * 32 + frag_row;
+        fa[fv] = *reinterpret_cast<const bf16x8*>(&sA[buf][swz(r, ch)]);
+      }
+#pragma unroll
+      for (int fr = 0; fr < T::FR; ++fr) {
+        const int r = wr * T::WR + fr * 32 + frag_row;
+        fb[fr] = *reinterpret_cast<const bf16x8*>(&sB[buf][swz(r, ch)]);
+      }
+#pragma unroll
+      for (int fv = 0; fv < T::FV; ++fv)
+#pragma unroll
+        for (int fr = 0; fr < T::FR; ++fr)
+          acc[fv][fr] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[fv], fb[fr], acc[fv][fr], 0, 0, 0);
+    }
+
+    if (ks == KT - 1) {
+      // Online reduction of this vocabulary tile.  Accumulator e of block
+      // (fv, fr) in this lane is vocabulary entry
+      //   v0 + fv*32 + 8*(e/4) + 4*(lane/32) + e%4
+      // of row wr*WR + fr*32 + lane%32; for a fixed lane these increase
+      // with (fv, e), so a strict '>' scan keeps the lowest index.
+      const int v0 = vt * T::BN + wv * T::WV + 4 * frag_half;
+      const bool full = (vt + 1) * T::BN <= V;
+#pragma unroll
+      for (int fr = 0; fr < T::FR; ++fr) {
+        float tm = -INFINITY;
+        int ta = 0;
+#pragma unroll
+        for (int fv = 0; fv < T::FV; ++fv)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int v = v0 + fv * 32 + 8 * (e >> 2) + (e & 3);
+            const float z = acc[fv][fr][e];
+            if ((full || v < V) && z > tm) {
+              tm = z;
+              ta = v;
+            }
+          }
+        if (tm != -INFINITY) {
+          const float mn = fmaxf(run_m[fr], tm);
+          const float sc = mn * kLog2e;
+          float sum = 0.f;
+#pragma unroll
+          for (int fv = 0; fv < T::FV; ++fv)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int v = v0 + fv * 32 + 8 * (e >> 2) + (e & 3);
+              const float t = __builtin_amdgcn_exp2f(fmaf(acc[fv][fr][e], kLog2e, -sc));
+              sum += (full || v < V) ? t : 0.f;
+            }
+          const float old = (run_m[fr] == -INFINITY) ? 0.f
+                                                     : run_s[fr] * __builtin_amdgcn_exp2f(run_m[fr] * kLog2e - sc);
+          run_s[fr] = old + sum;
+          run_a[fr] = (tm > run_m[fr]) ? ta : run_a[fr];
+          run_m[fr] = mn;
+        }
+      }
+#pragma unroll
+      for (int fv = 0; fv < T::FV; ++fv)
+#pragma unroll
+        for (int fr = 0; fr < T::FR; ++fr)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[fv][fr][e] = 0.f;
+    }
+
+    if (has_next) lstore(buf ^ 1);
+    __syncthreads();
+    vt = nvt;
+    ks = nks;
+  }
+
+  // Combine the two half-waves (same rows, interleaved vocabulary entries).
+#pragma unroll
+  for (int fr = 0; fr < T::FR; ++fr) {
+    const float m2 = __shfl_xor(run_m[fr], 32);
+    const int a2 = __shfl_xor(run_a[fr], 32);
+    const float s2 = __shfl_xor(run_s[fr], 32);
+    merge_state(run_m[fr], run_a[fr], run_s[fr], m2, a2, s2);
+  }
+
+  // Combine the WN waves that share rows, in wave order, through LDS.
+  float* xm = reinterpret_cast<float*>(&sA[0][0]);
+  int* xa = reinterpret_cast<int*>(xm + T::WN * T::BM);
+  float* xs = reinterpret_cast<float*>(xa + T::WN * T::BM);
+  static_assert(3 * T::WN * T::BM * 4 <= (int)sizeof(sA), "LDS exchange area too small");
+  if (frag_half == 0) {
+#pragma unroll
+    for (int fr = 0; fr < T::FR; ++fr) {
+      const int r = wr * T::WR + fr * 32 + frag_row;
+      xm[wv * T::BM + r] = run_m[fr];
+      xa[wv * T::BM + r] = run_a[fr];
+      xs[wv * T::BM + r] = run_s[fr];
+    }
+  }
+  __syncthreads();
+  for (int r = tid; r < T::BM; r += T::NT) {
+    float m = xm[r], s = xs[r];
+    int a = xa[r];
+#pragma unroll
+    for (int w = 1; w < T::WN; ++w) merge_state(m, a, s, xm[w * T::BM + r], xa[w * T::BM + r], xs[w * T::BM + r]);
+    const int row = row0 + r;
+    if (row < M) {
+      const size_t o = (size_t)row * (size_t)slices + (size_t)slice;
+      part_m[o] = m;
+      part_a[o] = a;
+      part_s[o] = s;
+    }
+  }
+}
+
+using LargeTile = Tile<kLargeBM, kLargeBN, 2, 4>;
+using SmallTile = Tile<kSmallBM, kSmallBN, 1, 4>;
+
+}  // namespace
+
+hipError_t launch_gemm_large(const uint16_t* W, const uint16_t* H, int d, int V, const int32_t* idx,
+                             const int32_t* ctr, int n_row_tiles, int slices, float* pm, int32_t* pa,
+                             float* ps, hipStream_t stream) {
+  const int n_vt = (V + LargeTile::BN - 1) / LargeTile::BN;
+  const int grid = n_row_tiles * slices;
+  hipLaunchKernelGGL(k_gemm_online<LargeTile>, dim3(grid), dim3(LargeTile::NT), 0, stream, W, H, d, V,
+                     idx, ctr, slices, n_vt, pm, pa, ps);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_small(const uint16_t* W, const uint16_t* H, int d, int V, const int32_t* idx,
+                             const int32_t* ctr, int slices, float* pm, int32_t* pa, float* ps,
+                             hipStream_t stream) {
+  const int n_vt = (V + SmallTile::BN - 1) / SmallTile::BN;
+  hipLaunchKernelGGL(k_gemm_online<SmallTile>, dim3(slices), dim3(SmallTile::NT), 0, stream, W, H, d, V,
+                     idx, ctr, slices, n_vt, pm, pa, ps);
+  return hipGetLastError();
+}
+
+}  // namespace dllm

@@ -1,0 +1,114 @@
+// Mask compaction: the ascending list of positions that still hold the mask
+// token inside the step's window ("mask-only logits", Mosaic Abstract), and
+// for block-wise decoding the first block of the window that still holds
+// one (Sparse-dLLM, Experiment "Memory": logits only for the current block).
+//
+// One workgroup of 1024 threads walks the window in chunks of 16 Ki
+// positions; each thread owns 16 consecutive mask bytes.  Within a wavefront
+// the exclusive prefix of the per-thread counts comes from ballots of the
+// count's bits (count = sum_b 2^b * bit_b, so the prefix is
+// sum_b 2^b * popcount(ballot(bit_b) & lanes-below)), across the 16 waves
+// from a small LDS table.  M and the window actually used go to ctr[0..2]
+// so no host synchronisation is needed before the next kernel.
+#include "readout_internal.h"
+
+namespace dllm {
+namespace {
+
+constexpr int kThreads = 1024;
+constexpr int kPerThread = 16;
+constexpr int kChunk = kThreads * kPerThread;
+
+__global__ __launch_bounds__(kThreads) void k_mask_compact(const uint8_t* __restrict__ mask,
+                                                           int64_t win_lo, int64_t win_hi,
+                                                           int64_t block, int32_t* __restrict__ idx,
+                                                           int32_t* __restrict__ ctr) {
+  __shared__ int s_first;
+  __shared__ int s_wave_total[kThreads / 64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  int lo = (int)win_lo, hi = (int)win_hi;
+
+  if (block > 0) {
+    // First masked position of the window (min over threads, chunk by chunk).
+    if (tid == 0) s_first = hi;
+    __syncthreads();
+    for (int base = lo; base < hi; base += kChunk) {
+      int mine = hi;
+      const int p0 = base + tid * kPerThread;
+#pragma unroll
+      for (int j = kPerThread - 1; j >= 0; --j) {
+        const int p = p0 + j;
+        if (p < hi && mask[p] != 0) mine = p;
+      }
+      if (mine < hi) atomicMin(&s_first, mine);
+      __syncthreads();
+      const bool found = s_first < hi;
+      __syncthreads();
+      if (found) break;
+    }
+    const int first = s_first;
+    if (first >= hi) {
+      lo = hi;
+    } else {
+      const int b = (int)((first - lo) / block);
+      const int64_t blo = (int64_t)lo + (int64_t)b * block;
+      const int64_t bhi = blo + block < (int64_t)hi ? blo + block : (int64_t)hi;
+      lo = (int)blo;
+      hi = (int)bhi;
+    }
+  }
+
+  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int running = 0;
+  for (int base = lo; base < hi; base += kChunk) {
+    const int p0 = base + tid * kPerThread;
+    unsigned bits = 0;
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      const int p = p0 + j;
+      if (p < hi && mask[p] != 0) bits |= 1u << j;
+    }
+    const int c = __popc(bits);
+    int pre = 0;
+#pragma unroll
+    for (int b = 0; b < 5; ++b) {
+      const unsigned long long bal = __ballot((c >> b) & 1);
+      pre += __popcll(bal & below) << b;
+    }
+    if (lane == 63) s_wave_total[wave] = pre + c;
+    __syncthreads();
+    int wave_off = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) {
+      const int t = s_wave_total[w];
+      wave_off += (w < wave) ? t : 0;
+      total += t;
+    }
+    int out = running + wave_off + pre;
+    while (bits) {
+      const int j = __ffs(bits) - 1;
+      bits &= bits - 1;
+      idx[out++] = p0 + j;
+    }
+    running += total;
+    __syncthreads();  // s_wave_total is rewritten by the next chunk
+  }
+  if (tid == 0) {
+    ctr[0] = running;
+    ctr[1] = lo;
+    ctr[2] = hi;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_mask_compact(const uint8_t* mask, int64_t win_lo, int64_t win_hi, int64_t block,
+                               int32_t* idx, int32_t* ctr, hipStream_t stream) {
+  hipLaunchKernelGGL(k_mask_compact, dim3(1), dim3(kThreads), 0, stream, mask, win_lo, win_hi, block,
+                     idx, ctr);
+  return hipGetLastError();
+}
+
+}  // namespace dllm

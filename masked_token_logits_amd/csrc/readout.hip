@@ -1,0 +1,194 @@
+// Host side of the C ABI: argument checks, workspace carving, choice of the
+// GEMM variant and launch of the four kernels on the handle's stream.
+#include "../../include/dllm_readout.h"
+#include "readout_internal.h"
+
+#include <stdio.h>
+#include <stdlib.h>
+
+#include <new>
+
+struct dllm_readout {
+  const uint16_t* W;
+  int64_t V, d, L_max;
+  int32_t k_max;
+  hipStream_t stream;
+  int cus;
+  int slices_override;
+  bool log;
+  dllm::Workspace ws;
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int64_t small_slice_count(int64_t V) {
+  const int64_t n_vt = (V + dllm::kSmallBN - 1) / dllm::kSmallBN;
+  return n_vt < dllm::kMaxSmallSlices ? n_vt : dllm::kMaxSmallSlices;
+}
+
+bool limits_ok(int64_t L_max, int64_t d, int64_t V, int32_t k_max) {
+  return L_max > 0 && L_max < (int64_t)1 << 31 && d > 0 && d < (int64_t)1 << 24 && V > 0 &&
+         V < (int64_t)1 << 31 && k_max >= 0 && k_max <= DLLM_K_MAX_LIMIT;
+}
+
+// Byte offsets of each workspace array; returns the total size.
+size_t carve(int64_t L_max, int64_t V, uint8_t* base, dllm::Workspace* ws) {
+  const int64_t part_cap_large = L_max * dllm::kMaxLargeSlices;
+  const int64_t part_cap_small = (int64_t)dllm::kSmallBM * small_slice_count(V);
+  const int64_t part_cap = part_cap_large > part_cap_small ? part_cap_large : part_cap_small;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = round_up(off + bytes);
+    return base ? base + o : nullptr;
+  };
+  dllm::Workspace w;
+  w.idx = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)L_max));
+  w.ctr = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * 16));
+  w.part_m = reinterpret_cast<float*>(take(sizeof(float) * (size_t)part_cap));
+  w.part_a = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)part_cap));
+  w.part_s = reinterpret_cast<float*>(take(sizeof(float) * (size_t)part_cap));
+  w.row_tok = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)L_max));
+  w.row_conf = reinterpret_cast<float*>(take(sizeof(float) * (size_t)L_max));
+  w.row_lse = reinterpret_cast<float*>(take(sizeof(float) * (size_t)L_max));
+  w.keys = reinterpret_cast<uint64_t*>(take(sizeof(uint64_t) * (size_t)L_max));
+  w.part_cap = part_cap;
+  if (ws) *ws = w;
+  return off;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Vocabulary slices for the compute-bound path: enough workgroups to fill
+// the device several times over, every slice at least one vocabulary tile.
+int choose_large_slices(int n_row_tiles, int64_t V, int cus) {
+  const int64_t n_vt = (V + dllm::kLargeBN - 1) / dllm::kLargeBN;
+  int64_t s = (4 * (int64_t)cus + n_row_tiles - 1) / n_row_tiles;
+  if (s < 1) s = 1;
+  if (s > dllm::kMaxLargeSlices) s = dllm::kMaxLargeSlices;
+  if (s > n_vt) s = n_vt;
+  return (int)s;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dllm_status_string(dllm_status s) {
+  switch (s) {
+    case DLLM_OK: return "ok";
+    case DLLM_ERR_INVALID_ARG: return "invalid argument";
+    case DLLM_ERR_UNSUPPORTED: return "unsupported argument (d % 8, pointer alignment or k_max)";
+    case DLLM_ERR_WORKSPACE: return "workspace missing or too small";
+    case DLLM_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+size_t dllm_masked_readout_workspace_bytes(int64_t L_max, int64_t d, int64_t V, int32_t k_max) {
+  if (!limits_ok(L_max, d, V, k_max)) return 0;
+  return carve(L_max, V, nullptr, nullptr);
+}
+
+dllm_status dllm_masked_readout_create(dllm_readout** out, const uint16_t* W_lm, int64_t V, int64_t d,
+                                       int64_t L_max, int32_t k_max, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  if (!out) return DLLM_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (!W_lm) return DLLM_ERR_INVALID_ARG;
+  if (k_max > DLLM_K_MAX_LIMIT) return DLLM_ERR_UNSUPPORTED;
+  if (!limits_ok(L_max, d, V, k_max)) return DLLM_ERR_INVALID_ARG;
+  if (d % 8 != 0 || !aligned16(W_lm)) return DLLM_ERR_UNSUPPORTED;
+  const size_t need = carve(L_max, V, nullptr, nullptr);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % kAlign) != 0) return DLLM_ERR_WORKSPACE;
+
+  dllm_readout* h = new (std::nothrow) dllm_readout;
+  if (!h) return DLLM_ERR_HIP;
+  h->W = W_lm;
+  h->V = V;
+  h->d = d;
+  h->L_max = L_max;
+  h->k_max = k_max;
+  h->stream = reinterpret_cast<hipStream_t>(stream);
+  h->cus = 0;  // queried at the first step
+  h->slices_override = 0;
+  const char* lg = getenv("DLLM_LOG");
+  h->log = lg && lg[0] == '1';
+  carve(L_max, V, reinterpret_cast<uint8_t*>(workspace), &h->ws);
+  *out = h;
+  return DLLM_OK;
+}
+
+dllm_status dllm_masked_readout_destroy(dllm_readout* h) {
+  delete h;
+  return DLLM_OK;
+}
+
+dllm_status dllm_masked_readout_set_slices(dllm_readout* h, int32_t slices) {
+  if (!h || slices < 0 || slices > dllm::kMaxLargeSlices) return DLLM_ERR_INVALID_ARG;
+  h->slices_override = slices;
+  return DLLM_OK;
+}
+
+dllm_status dllm_masked_readout_step(dllm_readout* h, const uint16_t* hidden, int64_t L, uint8_t* mask,
+                                     int32_t* tokens, int32_t k, int64_t win_lo, int64_t win_hi,
+                                     int64_t block, const dllm_step_out* out) {
+  if (!h || !hidden || !mask || !tokens) return DLLM_ERR_INVALID_ARG;
+  if (L <= 0 || L > h->L_max) return DLLM_ERR_INVALID_ARG;
+  if (k < 0 || k > h->k_max) return DLLM_ERR_INVALID_ARG;
+  if (win_lo < 0 || win_lo > win_hi || win_hi > L) return DLLM_ERR_INVALID_ARG;
+  if (block < 0) return DLLM_ERR_INVALID_ARG;
+  if (!aligned16(hidden)) return DLLM_ERR_UNSUPPORTED;
+  dllm_step_out o = {};
+  if (out) o = *out;
+  if (h->cus <= 0) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return DLLM_ERR_HIP;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      return DLLM_ERR_HIP;
+    h->cus = cus;
+  }
+
+  const dllm::Workspace& w = h->ws;
+  const int64_t span = win_hi - win_lo;
+  const int64_t rows_max = (block > 0 && block < span) ? block : span;  // upper bound on M
+  const int V = (int)h->V, d = (int)h->d;
+  hipStream_t st = h->stream;
+
+  if (dllm::launch_mask_compact(mask, win_lo, win_hi, block, w.idx, w.ctr, st) != hipSuccess)
+    return DLLM_ERR_HIP;
+
+  int slices = 0;
+  if (rows_max > 0) {
+    hipError_t e;
+    if (rows_max <= dllm::kSmallBM) {
+      slices = (int)small_slice_count(h->V);
+      e = dllm::launch_gemm_small(h->W, hidden, d, V, w.idx, w.ctr, slices, w.part_m, w.part_a, w.part_s, st);
+    } else {
+      const int n_rt = (int)((rows_max + dllm::kLargeBM - 1) / dllm::kLargeBM);
+      slices = h->slices_override > 0 ? h->slices_override : choose_large_slices(n_rt, h->V, h->cus);
+      const int64_t n_vt = (h->V + dllm::kLargeBN - 1) / dllm::kLargeBN;
+      if (slices > n_vt) slices = (int)n_vt;
+      e = dllm::launch_gemm_large(h->W, hidden, d, V, w.idx, w.ctr, n_rt, slices, w.part_m, w.part_a,
+                                  w.part_s, st);
+    }
+    if (h->log)
+      fprintf(stderr, "[dllm] step rows<=%lld path=%s slices=%d cus=%d\n", (long long)rows_max,
+              rows_max <= dllm::kSmallBM ? "small" : "large", slices, h->cus);
+    if (e != hipSuccess) return DLLM_ERR_HIP;
+    if (dllm::launch_merge(w.ctr, w.idx, w.part_m, w.part_a, w.part_s, slices, (int)rows_max, w.row_tok,
+                           w.row_conf, w.row_lse, w.keys, o.row_idx, o.row_tok, o.row_conf, o.row_lse,
+                           st) != hipSuccess)
+      return DLLM_ERR_HIP;
+  }
+  if (dllm::launch_topk_scatter(w.ctr, k, w.keys, w.idx, w.row_tok, mask, tokens, o.n_out, o.m_out,
+                                o.sel_idx, o.sel_tok, o.sel_conf, st) != hipSuccess)
+    return DLLM_ERR_HIP;
+  return DLLM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,130 @@
+"""The C-ABI library on the host: it loads, exports every declared symbol, and
+rejects bad arguments before touching the GPU.  No compute is launched."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import masked_token_logits_amd as mtl
+from masked_token_logits_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dllm_readout.h")
+
+# Fake but 256-byte aligned device addresses: validation never dereferences them.
+FAKE = 0x7F0000000000
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return mtl.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(dllm_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_three_calls():
+    names = declared_functions()
+    for n in ("dllm_masked_readout_create", "dllm_masked_readout_step", "dllm_masked_readout_destroy"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert sorted(_abi.EXPORTED) == declared_functions()
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert mtl.dllm_status_string(s)
+    assert mtl.dllm_status_string(99) == "unknown status"
+
+
+def test_workspace_bytes():
+    b = mtl.dllm_masked_readout_workspace_bytes(131072, 4096, 126464, 1024)
+    # O(L_max * slices) partials + O(L_max) row arrays; never O(L * V)
+    assert 0 < b < 131072 * 64 * 12 + 131072 * 40 + (1 << 20)
+    assert mtl.dllm_masked_readout_workspace_bytes(0, 4096, 126464, 8) == 0
+    assert mtl.dllm_masked_readout_workspace_bytes(10, 4096, 126464, -1) == 0
+    assert mtl.dllm_masked_readout_workspace_bytes(10, 4096, 0, 8) == 0
+    assert mtl.dllm_masked_readout_workspace_bytes(10, 4096, 126464, mtl.DLLM_K_MAX_LIMIT + 1) == 0
+    small = mtl.dllm_masked_readout_workspace_bytes(64, 4096, 126464, 8)
+    assert small >= 32 * ((126464 + 127) // 128) * 12
+
+
+def _create(**kw):
+    a = dict(W_lm=FAKE, V=1000, d=64, L_max=512, k_max=16, workspace=FAKE + 0x100000,
+             workspace_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return mtl.dllm_masked_readout_create(**a)
+
+
+def test_create_validation():
+    E = mtl
+    assert _create(W_lm=None)[0] == E.DLLM_ERR_INVALID_ARG
+    assert _create(V=0)[0] == E.DLLM_ERR_INVALID_ARG
+    assert _create(d=0)[0] == E.DLLM_ERR_INVALID_ARG
+    assert _create(L_max=0)[0] == E.DLLM_ERR_INVALID_ARG
+    assert _create(k_max=-1)[0] == E.DLLM_ERR_INVALID_ARG
+    assert _create(k_max=E.DLLM_K_MAX_LIMIT + 1)[0] == E.DLLM_ERR_UNSUPPORTED
+    assert _create(d=12)[0] == E.DLLM_ERR_UNSUPPORTED
+    assert _create(W_lm=FAKE + 8)[0] == E.DLLM_ERR_UNSUPPORTED
+    assert _create(workspace=None)[0] == E.DLLM_ERR_WORKSPACE
+    assert _create(workspace_bytes=100)[0] == E.DLLM_ERR_WORKSPACE
+    assert _create(workspace=FAKE + 0x100010)[0] == E.DLLM_ERR_WORKSPACE
+    st, h = _create()
+    assert st == E.DLLM_OK and h
+    assert mtl.dllm_masked_readout_destroy(h) == E.DLLM_OK
+
+
+def test_create_null_out(lib):
+    assert lib.dllm_masked_readout_create(None, FAKE, 10, 8, 10, 1, FAKE, 1 << 30, None) == mtl.DLLM_ERR_INVALID_ARG
+
+
+def test_step_validation_before_any_hip_call():
+    st, h = _create()
+    assert st == mtl.DLLM_OK
+    E = mtl
+    H, Mk, T = FAKE + 0x200000, FAKE + 0x300000, FAKE + 0x400000
+
+    def step(**kw):
+        a = dict(handle=h, hidden=H, L=256, mask=Mk, tokens=T, k=4, win_lo=0, win_hi=256, block=0)
+        a.update(kw)
+        return mtl.dllm_masked_readout_step(**a)
+
+    assert step(handle=None) == E.DLLM_ERR_INVALID_ARG
+    assert step(hidden=None) == E.DLLM_ERR_INVALID_ARG
+    assert step(mask=None) == E.DLLM_ERR_INVALID_ARG
+    assert step(tokens=None) == E.DLLM_ERR_INVALID_ARG
+    assert step(L=0) == E.DLLM_ERR_INVALID_ARG
+    assert step(L=513) == E.DLLM_ERR_INVALID_ARG
+    assert step(k=-1) == E.DLLM_ERR_INVALID_ARG
+    assert step(k=17) == E.DLLM_ERR_INVALID_ARG
+    assert step(win_lo=-1) == E.DLLM_ERR_INVALID_ARG
+    assert step(win_lo=10, win_hi=5) == E.DLLM_ERR_INVALID_ARG
+    assert step(win_hi=257) == E.DLLM_ERR_INVALID_ARG
+    assert step(block=-1) == E.DLLM_ERR_INVALID_ARG
+    assert step(hidden=H + 2) == E.DLLM_ERR_UNSUPPORTED
+    assert mtl.dllm_masked_readout_set_slices(h, -1) == E.DLLM_ERR_INVALID_ARG
+    assert mtl.dllm_masked_readout_set_slices(h, 65) == E.DLLM_ERR_INVALID_ARG
+    assert mtl.dllm_masked_readout_set_slices(h, 7) == E.DLLM_OK
+    assert mtl.dllm_masked_readout_set_slices(None, 1) == E.DLLM_ERR_INVALID_ARG
+    mtl.dllm_masked_readout_destroy(h)
+
+
+def test_step_without_device_reports_hip_error():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    st, h = _create()
+    r = mtl.dllm_masked_readout_step(h, FAKE + 0x200000, 256, FAKE + 0x300000, FAKE + 0x400000, 4, 0, 256, 0)
+    assert r == mtl.DLLM_ERR_HIP
+    mtl.dllm_masked_readout_destroy(h)
+
+
+def test_destroy_null():
+    assert mtl.dllm_masked_readout_destroy(None) == mtl.DLLM_OK
