@@ -1,0 +1,265 @@
+#!/usr/bin/env python3
+"""Benchmark of the masked-token readout on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llada|tiny|dream|lc_low|lc_high]
+
+A step is one denoising readout (compaction, masked LM-head GEMM with the
+streaming vocabulary reduction, merge, top-k commit) over one synthetic
+batch.  The default workload is the LLaDA-8B-like head (L=4096, d=4096,
+V=126464) decoded semi-autoregressively: the last 1024 positions are masked,
+blocks of 32, k=2 per step, 32 consecutive steps with the mask/token state
+carried on the device and the hidden states re-drawn every step; after 32
+steps the state is reset from a pristine device copy (inside the timed
+region).  All inputs are resident in HBM before timing starts.
+
+Prints ONE JSON line: masked tokens/s, the GEMM kernel's roofline (HIP
+events around its launch on the library's stream), and the fp64 CPU
+oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes as C
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+WORKLOADS = {"tiny": 1, "llada": 2, "dream": 3, "lc_low": 4, "lc_high": 5}
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+GEMM_SRC = os.path.join(ROOT, "masked_token_logits_amd", "csrc", "gemm_online.hip")
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+class Hip:
+    """The few HIP runtime calls the harness needs for kernel timing."""
+
+    def __init__(self):
+        self.lib = C.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        self.lib.hipEventDestroy.argtypes = [C.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+
+    def event(self) -> int:
+        e = C.c_void_p()
+        if self.lib.hipEventCreate(C.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return e.value
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        ms = C.c_float()
+        if self.lib.hipEventElapsedTime(C.byref(ms), C.c_void_p(a), C.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def destroy(self, e: int) -> None:
+        self.lib.hipEventDestroy(C.c_void_p(e))
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:  # pragma: no cover
+        return 1
+
+
+def traffic_from_profile(workload: str):
+    """HBM bytes per GEMM launch from the committed rocprofv3 counter summary,
+    or None when there is none or the GEMM source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"gemm_online_{workload}_hbm_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    src = hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()
+    m_sha = re.search(r"gemm_online\.hip sha256:\s*([0-9a-f]{64})", text)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_sha or not m_b or m_sha.group(1) != src:
+        return None
+    return float(m_b.group(1))
+
+
+def cpu_baseline(cfg, W, hidden_steps, mask0, tok0, n_rows_sample: int = 512):
+    """The fp64 oracle as it stands, on a bounded sample of the workload."""
+    import numpy as np
+
+    import oracle
+    t0 = time.perf_counter()
+    W64 = oracle.widen_bf16(W)
+    if cfg.steps > 1:
+        mask, tok = mask0, tok0
+        rows = 0
+        for t in range(cfg.steps):
+            lo, hi = cfg.win
+            r = oracle.readout_step(hidden_steps[t], W, mask, tok, cfg.k, lo, hi, cfg.block, W64=W64)
+            rows += r.M
+            mask, tok = r.mask, r.tokens
+        sample = f"all {cfg.steps} steps of one semi-AR pass ({rows} masked rows, full V each)"
+    elif cfg.L * cfg.V <= 8 * 1024 * 1024:
+        r = oracle.readout_step(hidden_steps[0], W, mask0, tok0, cfg.k, W64=W64)
+        rows = r.M
+        sample = f"the whole step ({rows} masked rows)"
+    else:
+        pos = np.flatnonzero(mask0)[:n_rows_sample]
+        oracle.readout_rows(hidden_steps[0], W, pos, W64=W64)
+        rows = len(pos)
+        sample = f"first {rows} masked rows of the step, full V each (rows/s scaled to masked tokens/s)"
+    dt = time.perf_counter() - t0
+    return dict(value=rows / dt, unit="masked tokens/s", cores=blas_threads(), kind="oracle",
+                sample=sample, seconds=round(dt, 3))
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=320)
+    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="llada")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
+    ap.add_argument("--slices", type=int, default=0, help="force the GEMM's vocabulary slice count")
+    args = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the readout would shard W_lm by vocabulary or the rows by sequence; see the design notes).",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import masked_token_logits_amd as mtl
+    import workloads as WL
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    mtl.load()
+    cfg = WL.CONFIGS[WORKLOADS[args.workload]]
+    dev = torch.device("cuda", 0)
+    t_gen = time.perf_counter()
+    W = WL.w_lm(cfg)
+    mask0, tok0 = WL.initial_state(cfg)
+    n_hidden = cfg.steps
+    hidden_steps = [WL.hidden(cfg, W, t)[0] for t in range(n_hidden)]
+    log(f"[bench] generated {args.workload} inputs in {time.perf_counter() - t_gen:.1f}s")
+
+    Wt = torch.from_numpy(W.view(np.int16)).to(dev)
+    Hts = [torch.from_numpy(h.view(np.int16)).to(dev) for h in hidden_steps]
+    m_pristine = torch.from_numpy(mask0).to(dev)
+    t_pristine = torch.from_numpy(tok0).to(dev)
+    mt = m_pristine.clone()
+    tt = t_pristine.clone()
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+
+    stream = torch.cuda.current_stream(dev)
+    rd = mtl.MaskedReadout(Wt, cfg.L, cfg.k, stream=stream)
+    if args.slices:
+        rd.set_slices(args.slices)
+    total = args.warmup + args.steps
+    m_slots = torch.zeros(total, dtype=torch.int32, device=dev)
+    lo, hi = cfg.win
+    hip = Hip()
+    ev = [(hip.event(), hip.event()) for _ in range(args.steps)]
+
+    def one(i: int, timed_index: int | None) -> None:
+        t = i % cfg.steps
+        if t == 0:
+            mt.copy_(m_pristine)
+            tt.copy_(t_pristine)
+        if timed_index is None:
+            mtl.dllm_masked_readout_set_gemm_events(rd.handle, None, None)
+        else:
+            a, b = ev[timed_index]
+            mtl.dllm_masked_readout_set_gemm_events(rd.handle, a, b)
+        out = {"m_out": m_slots.data_ptr() + 4 * i}
+        rd.step(Hts[t], mt, tt, cfg.k, lo, hi, cfg.block, out=out)
+
+    for i in range(args.warmup):
+        one(i, None)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for j in range(args.steps):
+        one(args.warmup + j, j)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    log(f"[bench] timed {args.steps} steps in {elapsed * 1e3:.2f} ms")
+
+    Ms = m_slots.cpu().numpy().astype(np.int64)
+    timed_M = Ms[args.warmup:]
+    masked_rows = int(timed_M.sum())
+    gemm_ms = np.array([hip.elapsed_ms(a, b) for a, b in ev])
+    for a, b in ev:
+        hip.destroy(a)
+        hip.destroy(b)
+    peak_mem = int(torch.cuda.max_memory_allocated())
+
+    d, V = cfg.d, cfg.V
+    small = (min(cfg.block, hi - lo) if cfg.block else hi - lo) <= 32
+    if small:
+        # HBM-bound: every launch streams all of W_lm once plus the gathered rows.
+        slices = (V + 127) // 128
+        bytes_per = V * d * 2 + timed_M * d * 2 + timed_M * slices * 12 + timed_M * 4
+        achieved = float(bytes_per.sum()) / (gemm_ms.sum() * 1e-3) / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4))
+    else:
+        flops = 2.0 * timed_M * d * V
+        achieved = float(flops.sum()) / (gemm_ms.sum() * 1e-3) / 1e12
+        roof = dict(bound="mfma", achieved=round(achieved, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=round(achieved / BF16_PEAK_TFLOPS, 4))
+    roof["traffic"] = traffic_from_profile(args.workload)
+    roof["kernel"] = "k_gemm_online<SmallTile>" if small else "k_gemm_persistent"
+    roof["kernel_avg_us"] = round(float(gemm_ms.mean()) * 1e3, 2)
+
+    value = masked_rows / elapsed
+    rec = {
+        "metric": "masked tokens/sec per denoise step",
+        "value": round(value, 1),
+        "unit": "masked tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; random-init LM head of the named shape, no checkpoint or dataset)",
+        "config": {
+            "workload": f"{cfg.name} (L={cfg.L}, d={d}, V={V}, k={cfg.k}"
+                        + (f", block={cfg.block}, {cfg.steps}-step semi-AR loop" if cfg.block else "") + ")",
+            "L": cfg.L, "d": d, "V": V, "k": cfg.k,
+            "masked_rows_timed": masked_rows,
+            "peak_mem_bytes": peak_mem,
+            "full_logits_fp32_bytes": cfg.L * V * 4,
+            "workspace_bytes": int(rd.workspace.numel()),
+            "parallelism": "single GPU",
+        },
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        rec["cpu_baseline"] = cpu_baseline(cfg, W, hidden_steps, mask0, tok0)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+    rd.close()
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -150,6 +150,16 @@ const char *dllm_status_string(dllm_status s);
  */
 dllm_status dllm_masked_readout_set_slices(dllm_readout *h, int32_t slices);
 
+/*
+ * Benchmark hook: when both are non-NULL, every later step records
+ * ev_before (a hipEvent_t) on the handle's stream right before it queues the
+ * GEMM kernel and ev_after right after it, so hipEventElapsedTime gives that
+ * kernel's duration.  The events are created and owned by the caller; pass
+ * NULL, NULL to stop.  DLLM_ERR_INVALID_ARG if h is NULL or only one event
+ * is given.
+ */
+dllm_status dllm_masked_readout_set_gemm_events(dllm_readout *h, void *ev_before, void *ev_after);
+
 #ifdef __cplusplus
 }
 #endif

@@ -22,6 +22,7 @@ from ._abi import (  # noqa: F401
     DllmError,
     dllm_masked_readout_create,
     dllm_masked_readout_destroy,
+    dllm_masked_readout_set_gemm_events,
     dllm_masked_readout_set_slices,
     dllm_masked_readout_step,
     dllm_masked_readout_workspace_bytes,

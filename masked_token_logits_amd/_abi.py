@@ -27,6 +27,7 @@ EXPORTED = (
     "dllm_masked_readout_destroy",
     "dllm_status_string",
     "dllm_masked_readout_set_slices",
+    "dllm_masked_readout_set_gemm_events",
 )
 
 
@@ -70,6 +71,8 @@ def load(path: str = LIB_PATH):
     lib.dllm_status_string.argtypes = [C.c_int]
     lib.dllm_masked_readout_set_slices.restype = C.c_int
     lib.dllm_masked_readout_set_slices.argtypes = [C.c_void_p, C.c_int32]
+    lib.dllm_masked_readout_set_gemm_events.restype = C.c_int
+    lib.dllm_masked_readout_set_gemm_events.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p]
     _lib = lib
     return lib
 
@@ -129,3 +132,7 @@ def dllm_masked_readout_destroy(handle) -> int:
 
 def dllm_masked_readout_set_slices(handle, slices: int) -> int:
     return load().dllm_masked_readout_set_slices(handle, slices)
+
+
+def dllm_masked_readout_set_gemm_events(handle, ev_before, ev_after) -> int:
+    return load().dllm_masked_readout_set_gemm_events(handle, ev_before, ev_after)

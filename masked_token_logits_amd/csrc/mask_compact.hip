@@ -10,6 +10,11 @@
 // sum_b 2^b * popcount(ballot(bit_b) & lanes-below)), across the 16 waves
 // from a small LDS table.  M and the window actually used go to ctr[0..2]
 // so no host synchronisation is needed before the next kernel.
+//
+// The same kernel then fixes how the GEMM splits the work, now that M is
+// known: for the persistent GEMM it picks the vocabulary slice count S that
+// minimises (rounds of the persistent grid) x (longest item), each thread
+// scoring one candidate and an LDS atomicMin choosing (ties: fewer slices).
 #include "readout_internal.h"
 
 namespace dllm {
@@ -21,9 +26,11 @@ constexpr int kChunk = kThreads * kPerThread;
 
 __global__ __launch_bounds__(kThreads) void k_mask_compact(const uint8_t* __restrict__ mask,
                                                            int64_t win_lo, int64_t win_hi,
-                                                           int64_t block, int32_t* __restrict__ idx,
+                                                           int64_t block, PlanParams plan,
+                                                           int32_t* __restrict__ idx,
                                                            int32_t* __restrict__ ctr) {
   __shared__ int s_first;
+  __shared__ unsigned long long s_best;
   __shared__ int s_wave_total[kThreads / 64];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -95,18 +102,39 @@ __global__ __launch_bounds__(kThreads) void k_mask_compact(const uint8_t* __rest
     running += total;
     __syncthreads();  // s_wave_total is rewritten by the next chunk
   }
+  const int M = running;
+  const int n_rt = (M + plan.tile_rows - 1) / plan.tile_rows;
+  int S = plan.fixed_slices;
+  if (S <= 0) {
+    if (tid == 0) s_best = ~0ull;
+    __syncthreads();
+    if (n_rt > 0) {
+      for (int c = tid + 1; c <= plan.max_slices && c <= plan.n_vt; c += kThreads) {
+        if ((int64_t)n_rt * plan.tile_rows * c > plan.part_cap) break;
+        const int64_t items = (int64_t)n_rt * c;
+        const int64_t rounds = (items + plan.grid - 1) / plan.grid;
+        const int64_t len = (plan.n_vt + c - 1) / c;  // vocabulary tiles of the longest item
+        const unsigned long long cost = (unsigned long long)(rounds * (4 * len + 1));
+        atomicMin(&s_best, (cost << 20) | (unsigned long long)c);
+      }
+    }
+    __syncthreads();
+    S = (s_best == ~0ull) ? 1 : (int)(s_best & 0xFFFFF);
+  }
   if (tid == 0) {
-    ctr[0] = running;
+    ctr[0] = M;
     ctr[1] = lo;
     ctr[2] = hi;
+    ctr[3] = S;
+    ctr[4] = n_rt;
   }
 }
 
 }  // namespace
 
 hipError_t launch_mask_compact(const uint8_t* mask, int64_t win_lo, int64_t win_hi, int64_t block,
-                               int32_t* idx, int32_t* ctr, hipStream_t stream) {
-  hipLaunchKernelGGL(k_mask_compact, dim3(1), dim3(kThreads), 0, stream, mask, win_lo, win_hi, block,
+                               PlanParams plan, int32_t* idx, int32_t* ctr, hipStream_t stream) {
+  hipLaunchKernelGGL(k_mask_compact, dim3(1), dim3(kThreads), 0, stream, mask, win_lo, win_hi, block, plan,
                      idx, ctr);
   return hipGetLastError();
 }

@@ -40,11 +40,12 @@ constexpr int kMergeWaves = 4;
 
 __global__ __launch_bounds__(kMergeWaves * 64) void k_merge(
     const int32_t* __restrict__ ctr, const int32_t* __restrict__ idx, const float* __restrict__ pm,
-    const int32_t* __restrict__ pa, const float* __restrict__ ps, int slices,
+    const int32_t* __restrict__ pa, const float* __restrict__ ps,
     int32_t* __restrict__ row_tok, float* __restrict__ row_conf, float* __restrict__ row_lse,
     uint64_t* __restrict__ keys, int32_t* o_row_idx, int32_t* o_row_tok, float* o_row_conf,
     float* o_row_lse) {
   const int M = ctr[0];
+  const int slices = ctr[3];
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * kMergeWaves + (threadIdx.x >> 6);
   if (row >= M) return;
@@ -177,12 +178,12 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_scatter(
 }  // namespace
 
 hipError_t launch_merge(const int32_t* ctr, const int32_t* idx, const float* pm, const int32_t* pa,
-                        const float* ps, int slices, int max_rows, int32_t* row_tok, float* row_conf,
+                        const float* ps, int max_rows, int32_t* row_tok, float* row_conf,
                         float* row_lse, uint64_t* keys, int32_t* o_row_idx, int32_t* o_row_tok,
                         float* o_row_conf, float* o_row_lse, hipStream_t stream) {
   const int grid = (max_rows + kMergeWaves - 1) / kMergeWaves;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_merge, dim3(grid), dim3(kMergeWaves * 64), 0, stream, ctr, idx, pm, pa, ps, slices,
+  hipLaunchKernelGGL(k_merge, dim3(grid), dim3(kMergeWaves * 64), 0, stream, ctr, idx, pm, pa, ps,
                      row_tok, row_conf, row_lse, keys, o_row_idx, o_row_tok, o_row_conf, o_row_lse);
   return hipGetLastError();
 }

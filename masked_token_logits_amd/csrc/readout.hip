@@ -16,6 +16,7 @@ struct dllm_readout {
   int cus;
   int slices_override;
   bool log;
+  hipEvent_t ev_before, ev_after;
   dllm::Workspace ws;
 };
 
@@ -37,7 +38,9 @@ bool limits_ok(int64_t L_max, int64_t d, int64_t V, int32_t k_max) {
 
 // Byte offsets of each workspace array; returns the total size.
 size_t carve(int64_t L_max, int64_t V, uint8_t* base, dllm::Workspace* ws) {
-  const int64_t part_cap_large = L_max * dllm::kMaxLargeSlices;
+  // whole 256-row tiles times the largest slice count, so any plan with S <= 64 fits
+  const int64_t part_cap_large = (L_max + dllm::kLargeBM - 1) / dllm::kLargeBM * dllm::kLargeBM *
+                                 dllm::kMaxLargeSlices;
   const int64_t part_cap_small = (int64_t)dllm::kSmallBM * small_slice_count(V);
   const int64_t part_cap = part_cap_large > part_cap_small ? part_cap_large : part_cap_small;
   size_t off = 0;
@@ -116,6 +119,8 @@ dllm_status dllm_masked_readout_create(dllm_readout** out, const uint16_t* W_lm,
   h->stream = reinterpret_cast<hipStream_t>(stream);
   h->cus = 0;  // queried at the first step
   h->slices_override = 0;
+  h->ev_before = nullptr;
+  h->ev_after = nullptr;
   const char* lg = getenv("DLLM_LOG");
   h->log = lg && lg[0] == '1';
   carve(L_max, V, reinterpret_cast<uint8_t*>(workspace), &h->ws);
@@ -131,6 +136,13 @@ dllm_status dllm_masked_readout_destroy(dllm_readout* h) {
 dllm_status dllm_masked_readout_set_slices(dllm_readout* h, int32_t slices) {
   if (!h || slices < 0 || slices > dllm::kMaxLargeSlices) return DLLM_ERR_INVALID_ARG;
   h->slices_override = slices;
+  return DLLM_OK;
+}
+
+dllm_status dllm_masked_readout_set_gemm_events(dllm_readout* h, void* ev_before, void* ev_after) {
+  if (!h || ((ev_before == nullptr) != (ev_after == nullptr))) return DLLM_ERR_INVALID_ARG;
+  h->ev_before = reinterpret_cast<hipEvent_t>(ev_before);
+  h->ev_after = reinterpret_cast<hipEvent_t>(ev_after);
   return DLLM_OK;
 }
 
@@ -159,28 +171,57 @@ dllm_status dllm_masked_readout_step(dllm_readout* h, const uint16_t* hidden, in
   const int V = (int)h->V, d = (int)h->d;
   hipStream_t st = h->stream;
 
-  if (dllm::launch_mask_compact(mask, win_lo, win_hi, block, w.idx, w.ctr, st) != hipSuccess)
+  // Choose the GEMM variant from the host-known bound on M; the slice count
+  // of the persistent variant is fixed on the device once M is known.
+  enum { kSmall, kPersistent, kStreaming } path;
+  const int64_t n_vt_large = (h->V + dllm::kLargeBN - 1) / dllm::kLargeBN;
+  dllm::PlanParams plan = {};
+  int n_rt = 0;
+  if (rows_max <= dllm::kSmallBM) {
+    path = kSmall;
+    plan.fixed_slices = (int)small_slice_count(h->V);
+    plan.tile_rows = dllm::kSmallBM;
+  } else if (h->d % dllm::kPersistBK == 0) {
+    path = kPersistent;
+    int so = h->slices_override;
+    if (so > n_vt_large) so = (int)n_vt_large;
+    plan.fixed_slices = so;
+    plan.tile_rows = dllm::kPersistBM;
+    plan.n_vt = (int)n_vt_large;
+    plan.grid = h->cus;
+    plan.max_slices = 1024;
+    plan.part_cap = w.part_cap;
+  } else {
+    path = kStreaming;
+    n_rt = (int)((rows_max + dllm::kLargeBM - 1) / dllm::kLargeBM);
+    int sl = h->slices_override > 0 ? h->slices_override : choose_large_slices(n_rt, h->V, h->cus);
+    if (sl > n_vt_large) sl = (int)n_vt_large;
+    plan.fixed_slices = sl;
+    plan.tile_rows = dllm::kLargeBM;
+  }
+  if (dllm::launch_mask_compact(mask, win_lo, win_hi, block, plan, w.idx, w.ctr, st) != hipSuccess)
     return DLLM_ERR_HIP;
 
-  int slices = 0;
   if (rows_max > 0) {
     hipError_t e;
-    if (rows_max <= dllm::kSmallBM) {
-      slices = (int)small_slice_count(h->V);
-      e = dllm::launch_gemm_small(h->W, hidden, d, V, w.idx, w.ctr, slices, w.part_m, w.part_a, w.part_s, st);
-    } else {
-      const int n_rt = (int)((rows_max + dllm::kLargeBM - 1) / dllm::kLargeBM);
-      slices = h->slices_override > 0 ? h->slices_override : choose_large_slices(n_rt, h->V, h->cus);
-      const int64_t n_vt = (h->V + dllm::kLargeBN - 1) / dllm::kLargeBN;
-      if (slices > n_vt) slices = (int)n_vt;
-      e = dllm::launch_gemm_large(h->W, hidden, d, V, w.idx, w.ctr, n_rt, slices, w.part_m, w.part_a,
+    if (h->ev_before && hipEventRecord(h->ev_before, st) != hipSuccess) return DLLM_ERR_HIP;
+    if (path == kSmall) {
+      e = dllm::launch_gemm_small(h->W, hidden, d, V, w.idx, w.ctr, plan.fixed_slices, w.part_m, w.part_a,
                                   w.part_s, st);
+    } else if (path == kPersistent) {
+      e = dllm::launch_gemm_persistent(h->W, hidden, d, V, w.idx, w.ctr, h->cus, w.part_m, w.part_a, w.part_s,
+                                       st);
+    } else {
+      e = dllm::launch_gemm_large(h->W, hidden, d, V, w.idx, w.ctr, n_rt, plan.fixed_slices, w.part_m,
+                                  w.part_a, w.part_s, st);
     }
     if (h->log)
       fprintf(stderr, "[dllm] step rows<=%lld path=%s slices=%d cus=%d\n", (long long)rows_max,
-              rows_max <= dllm::kSmallBM ? "small" : "large", slices, h->cus);
+              path == kSmall ? "small" : path == kPersistent ? "persistent" : "streaming", plan.fixed_slices,
+              h->cus);
     if (e != hipSuccess) return DLLM_ERR_HIP;
-    if (dllm::launch_merge(w.ctr, w.idx, w.part_m, w.part_a, w.part_s, slices, (int)rows_max, w.row_tok,
+    if (h->ev_after && hipEventRecord(h->ev_after, st) != hipSuccess) return DLLM_ERR_HIP;
+    if (dllm::launch_merge(w.ctr, w.idx, w.part_m, w.part_a, w.part_s, (int)rows_max, w.row_tok,
                            w.row_conf, w.row_lse, w.keys, o.row_idx, o.row_tok, o.row_conf, o.row_lse,
                            st) != hipSuccess)
       return DLLM_ERR_HIP;

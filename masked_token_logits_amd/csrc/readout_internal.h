@@ -10,7 +10,8 @@ namespace dllm {
 // Layout of the device workspace, carved by the host at create time.
 struct Workspace {
   int32_t* idx;        // [L_max]   candidate positions, ascending (compaction output)
-  int32_t* ctr;        // [16]      ctr[0] = M, ctr[1] = lo, ctr[2] = hi of the candidate window
+  int32_t* ctr;        // [16]      ctr[0] = M, ctr[1] = lo, ctr[2] = hi of the candidate window,
+                       //           ctr[3] = vocabulary slices S of this step, ctr[4] = row tiles
   float* part_m;       // [part_cap] per (row, slice) running max logit
   int32_t* part_a;     // [part_cap] per (row, slice) argmax vocabulary index
   float* part_s;       // [part_cap] per (row, slice) sum of exp(z - part_m)
@@ -29,20 +30,41 @@ constexpr int kMaxLargeSlices = 64;
 constexpr int kMaxSmallSlices = 2048;
 constexpr int kTopkCap = 4096;          // largest k the selection kernel holds in LDS
 
+// How the step's work is split, decided on the device once M is known.
+//   fixed_slices > 0: S = fixed_slices (rows are one tile of `tile_rows`).
+//   fixed_slices == 0: persistent GEMM with `grid` workgroups; S is chosen
+//   so that the n_rt * S (row tile, slice) items fill whole rounds of the
+//   grid with equally long items, with n_rt * tile_rows * S <= part_cap.
+struct PlanParams {
+  int fixed_slices;
+  int tile_rows;
+  int n_vt;        // vocabulary tiles
+  int grid;        // persistent workgroups
+  int max_slices;
+  int64_t part_cap;
+};
+
 // Kernel launchers (each queues exactly one kernel on `stream`).
 hipError_t launch_mask_compact(const uint8_t* mask, int64_t win_lo, int64_t win_hi, int64_t block,
-                               int32_t* idx, int32_t* ctr, hipStream_t stream);
+                               PlanParams plan, int32_t* idx, int32_t* ctr, hipStream_t stream);
 
 hipError_t launch_gemm_large(const uint16_t* W, const uint16_t* H, int d, int V, const int32_t* idx,
                              const int32_t* ctr, int n_row_tiles, int slices, float* pm, int32_t* pa,
                              float* ps, hipStream_t stream);
+
+// Persistent compute-bound variant (d % 32 == 0): `grid` workgroups walk the
+// (row tile, slice) items of the device-side plan in ctr[3], ctr[4].
+constexpr int kPersistBM = 256, kPersistBN = 256, kPersistBK = 32, kPersistStages = 4;
+hipError_t launch_gemm_persistent(const uint16_t* W, const uint16_t* H, int d, int V, const int32_t* idx,
+                                  const int32_t* ctr, int grid, float* pm, int32_t* pa, float* ps,
+                                  hipStream_t stream);
 
 hipError_t launch_gemm_small(const uint16_t* W, const uint16_t* H, int d, int V, const int32_t* idx,
                              const int32_t* ctr, int slices, float* pm, int32_t* pa, float* ps,
                              hipStream_t stream);
 
 hipError_t launch_merge(const int32_t* ctr, const int32_t* idx, const float* pm, const int32_t* pa,
-                        const float* ps, int slices, int max_rows, int32_t* row_tok, float* row_conf,
+                        const float* ps, int max_rows, int32_t* row_tok, float* row_conf,
                         float* row_lse, uint64_t* keys, int32_t* o_row_idx, int32_t* o_row_tok,
                         float* o_row_conf, float* o_row_lse, hipStream_t stream);
 
