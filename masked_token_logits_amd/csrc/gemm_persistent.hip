@@ -15,9 +15,12 @@
 //     no VGPR staging.  BK = 32, a 4-deep ring of (W tile, hidden tile)
 //     stages (128 KiB of the 160 KiB LDS): three stages are in flight while
 //     one is consumed.  Waits are explicit (s_waitcnt vmcnt(N) + s_barrier)
-//     so the compiler's conservative vmcnt(0) never drains the ring.
-//   * 16-byte chunks are XOR-swizzled by row ((row >> 1) & 3) so that the
-//     ds_read_b128 fragment loads are bank-conflict free; the swizzle is
+//     so the compiler's conservative vmcnt(0) never drains the ring.  The
+//     barrier sits between the two 16-deep K steps of a stage, so the next
+//     stage's first fragments load while the current stage's second batch
+//     of 16 MFMAs runs: LDS latency never stalls the matrix pipe.
+//   * 16-byte chunks are XOR-swizzled by row so that the ds_read_b128
+//     fragment loads are bank-conflict free; the swizzle is
 //     applied by choosing each lane's global source chunk, since a DMA lane
 //     always lands at LDS base + 16 * lane.
 //   * The gather is fused: the hidden rows of a row tile are resolved once
@@ -26,12 +29,13 @@
 //     plan (ctr[3] = slices, ctr[4] = row tiles) written by the compaction
 //     kernel once M is known.  Workgroup b takes items q(b), q(b) + G, ...,
 //     with q(b) remapped so that the 32 workgroups of one XCD take 32
-//     consecutive items (neighbouring slices of the same row tiles): they
-//     share hidden tiles in their XCD's L2, and all XCDs walk the same W_lm
-//     tiles at the same time (shared in the Infinity Cache).
+//     consecutive items, and items ordered (item_coords) so that those 32
+//     form a 4 row-tile x 8 slice block and all XCDs share the same slices.
 #include "readout_internal.h"
 
 #include <math.h>
+
+#include <type_traits>
 
 namespace dllm {
 namespace {
@@ -55,6 +59,41 @@ __device__ __forceinline__ int xcd_remap(int bid, int grid) {
   const int per = grid / kXcd, rem = grid % kXcd;
   const int x = bid % kXcd, loc = bid / kXcd;
   return (x < rem) ? x * (per + 1) + loc : rem * (per + 1) + (x - rem) * per + loc;
+}
+
+// Work-item order.  Items are (row tile, vocabulary slice) pairs, taken in
+// blocks of 32 row tiles x 8 slices; inside a block, sub-blocks of 4 row
+// tiles x 8 slices with the row tile fastest.  With 256 workgroups, a round
+// of the persistent grid is one block, and the 32 workgroups of each XCD
+// (consecutive positions after xcd_remap) hold one 4 x 8 sub-block: in an
+// XCD's L2 every hidden tile is shared by 8 workgroups and every W_lm tile
+// by 4, and all 8 XCDs stream the same 8 W_lm slices at the same time, so
+// each W_lm tile leaves HBM once per 32 row tiles.  Edge blocks shrink; the
+// map is a bijection onto [0, n_rt) x [0, S).
+constexpr int kGroupRows = 32, kGroupSlices = 8, kSubRows = 4;
+
+__device__ __forceinline__ void item_coords(int e, int n_rt, int S, int& rt, int& slice) {
+  const int g = e / (kGroupRows * S);
+  const int e1 = e - g * kGroupRows * S;
+  const int rb = min(kGroupRows, n_rt - g * kGroupRows);
+  const int h = e1 / (rb * kGroupSlices);
+  const int el = e1 - h * rb * kGroupSlices;
+  const int cb = min(kGroupSlices, S - h * kGroupSlices);
+  const int nsub = rb / kSubRows;
+  int r, c;
+  if (el < nsub * kSubRows * cb) {
+    const int sg = el / (kSubRows * cb);
+    const int rem = el - sg * kSubRows * cb;
+    c = rem / kSubRows;
+    r = sg * kSubRows + (rem - c * kSubRows);
+  } else {
+    const int rem = el - nsub * kSubRows * cb;
+    const int rr = rb - nsub * kSubRows;
+    c = rem / rr;
+    r = nsub * kSubRows + (rem - c * rr);
+  }
+  rt = g * kGroupRows + r;
+  slice = h * kGroupSlices + c;
 }
 
 __device__ __forceinline__ void merge_state(float& m, int& a, float& s, float m2, int a2, float s2) {
@@ -102,62 +141,77 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_persistent(const uint16_t* __res
   const int wr = wave >> 1;   // rows [wr * 128, +128)
   const int wv = wave & 1;    // vocabulary [wv * 128, +128)
 
-  // DMA lane geometry: lane -> row (lane / 4) of a 16-row block, LDS chunk
-  // position lane % 4, global chunk = position ^ ((row >> 1) & 3).
+  // LDS layout of a [256][32] bf16 operand tile: row r holds its four 16-byte
+  // chunks at positions chunk ^ f(r), f(r) = (r >> 2) & 3.  A ds_read_b128
+  // phase serves 16 lanes = 16 consecutive rows of one chunk; rows r and r+4k
+  // share a 64-byte bank quarter ((r & 3) * 64 of each 256 bytes) and f gives
+  // them distinct 16-byte positions, so the 16 reads hit 64 distinct banks
+  // (measured: no LDS bank conflicts).  DMA lane geometry: lane -> row
+  // (lane / 4) of a 16-row block, LDS position lane % 4, global chunk =
+  // position ^ f(row) = position ^ ((lane >> 4) & 3).
   const int dma_row = lane >> 2;
-  const int dma_chunk = (lane & 3) ^ ((lane >> 3) & 3);
+  const int dma_chunk = (lane & 3) ^ ((lane >> 4) & 3);
   // Fragment geometry: lane -> row lane % 32 of a 32-row block, K half lane / 32.
   const int frag_row = lane & 31;
   const int frag_half = lane >> 5;
-  const int frag_swz = (lane >> 1) & 3;
+  const int frag_swz = (lane >> 2) & 3;  // f(row) for row = 32-aligned base + lane % 32
 
   for (int e = xcd_remap(blockIdx.x, gridDim.x); e < n_items; e += gridDim.x) {
-    const int rt = e / S;
-    const int slice = e - rt * S;
+    int rt, slice;
+    item_coords(e, n_rt, S, rt, slice);
     const int row0 = rt * BM;
     const int vt_lo = (int)(((int64_t)slice * n_vt) / S);
     const int vt_hi = (int)(((int64_t)(slice + 1) * n_vt) / S);
-    const int total = (vt_hi - vt_lo) * KT;
 
-    // Hidden-row sources of this lane's B DMAs (rows past M repeat row M-1).
-    const uint16_t* hsrc[DMA_PER_OPERAND];
+    // DMA sources as 32-bit byte offsets from uniform 64-bit bases (the host
+    // only takes this path when W_lm and hidden each span < 4 GiB), so the
+    // loads use scalar-base addressing and each costs one VGPR.
+    // Hidden rows past M repeat row M-1.
+    uint32_t hoff[DMA_PER_OPERAND];
 #pragma unroll
     for (int i = 0; i < DMA_PER_OPERAND; ++i) {
       int r = row0 + (wave + 4 * i) * DMA_ROWS + dma_row;
       r = r < M ? r : M - 1;
-      hsrc[i] = H + (size_t)idx[r] * (size_t)d + dma_chunk * 8;
+      hoff[i] = ((uint32_t)idx[r] * (uint32_t)d + (uint32_t)(dma_chunk * 8)) * 2u;
     }
-
-    // Issue bookkeeping: the next stage to load is (iss_vt, iss_k0) into ring slot iss_slot.
-    int issued = 0, iss_vt = vt_lo, iss_k0 = 0, iss_slot = 0;
-    const uint16_t* wsrc[DMA_PER_OPERAND];
-    auto set_w_rows = [&](int vt) {
+    uint32_t woff[DMA_PER_OPERAND];
 #pragma unroll
-      for (int i = 0; i < DMA_PER_OPERAND; ++i) {
-        int v = vt * BN + (wave + 4 * i) * DMA_ROWS + dma_row;
-        v = v < V ? v : V - 1;
-        wsrc[i] = W + (size_t)v * (size_t)d + dma_chunk * 8;
-      }
-    };
-    set_w_rows(iss_vt);
+    for (int i = 0; i < DMA_PER_OPERAND; ++i) woff[i] = (uint32_t)(((wave + 4 * i) * DMA_ROWS + dma_row) * d + dma_chunk * 8) * 2u;
+    const char* Hb = reinterpret_cast<const char*>(H);
+
+    // Issue bookkeeping: the next stage to load is (iss_vt, iss_k0) into
+    // ring slot iss_slot.  Every stage issues exactly one stage of DMAs, also
+    // past the item's last stage: those re-read the item's last W_lm tile
+    // (valid memory) into the slot just freed and are never consumed.  The
+    // stage body is then branch-free (so DMAs and fragment loads interleave
+    // with the MFMAs) and always has two stages in flight behind the one it
+    // waits for.  The item's final vmcnt(0) drains the extra DMAs.
+    int iss_vt = vt_lo, iss_k0 = 0, iss_slot = 0;
     auto issue_next = [&]() {
       uint16_t* sa = &lds[iss_slot][0][0] + wave * DMA_ROWS * BK;
       uint16_t* sb = &lds[iss_slot][1][0] + wave * DMA_ROWS * BK;
+      // Rows past V (last vocabulary tile only) re-read row 0 of the tile;
+      // the epilogue drops their logits.
+      const int vbase = (iss_vt < vt_hi ? iss_vt : vt_hi - 1) * BN;
+      const char* Wb = reinterpret_cast<const char*>(W + (size_t)vbase * (size_t)d + iss_k0);
+      const bool wfull = vbase + BN <= V;
+#pragma unroll
+      for (int i = 0; i < DMA_PER_OPERAND; ++i) {
+        const uint32_t o = (wfull || vbase + (wave + 4 * i) * DMA_ROWS + dma_row < V) ? woff[i]
+                                                                                       : (uint32_t)(dma_chunk * 16);
+        __builtin_amdgcn_global_load_lds((const void*)(Wb + o), (LDS_AS void*)(sa + i * 4 * DMA_ROWS * BK), 16, 0,
+                                         0);
+      }
+      const char* Hk = Hb + (size_t)iss_k0 * 2u;
 #pragma unroll
       for (int i = 0; i < DMA_PER_OPERAND; ++i)
-        __builtin_amdgcn_global_load_lds((const void*)(wsrc[i] + iss_k0),
-                                         (LDS_AS void*)(sa + i * 4 * DMA_ROWS * BK), 16, 0, 0);
-#pragma unroll
-      for (int i = 0; i < DMA_PER_OPERAND; ++i)
-        __builtin_amdgcn_global_load_lds((const void*)(hsrc[i] + iss_k0),
-                                         (LDS_AS void*)(sb + i * 4 * DMA_ROWS * BK), 16, 0, 0);
-      ++issued;
+        __builtin_amdgcn_global_load_lds((const void*)(Hk + hoff[i]), (LDS_AS void*)(sb + i * 4 * DMA_ROWS * BK),
+                                         16, 0, 0);
       iss_slot = (iss_slot + 1) & (NST - 1);
       iss_k0 += BK;
       if (iss_k0 == d) {
         iss_k0 = 0;
         ++iss_vt;
-        if (iss_vt < vt_hi) set_w_rows(iss_vt);
       }
     };
 
@@ -170,86 +224,123 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_persistent(const uint16_t* __res
       run_a[fr] = 0;
     }
 
-    // Prologue: stages 0 .. NST-2 in flight.
+    // Fragment loads of K step kk (0/1) of ring slot `slot`.
+    auto load_frags = [&](int slot, int kk, bf16x8* fa, bf16x8* fb) {
+      const uint16_t* sa = &lds[slot][0][0];
+      const uint16_t* sb = &lds[slot][1][0];
+      const int chunk = ((kk * 2 + frag_half) ^ frag_swz) * 8;
 #pragma unroll
-    for (int p = 0; p < NST - 1; ++p)
-      if (issued < total) issue_next();
+      for (int f = 0; f < 4; ++f) {
+        fa[f] = *reinterpret_cast<const bf16x8*>(sa + (wv * 128 + f * 32 + frag_row) * BK + chunk);
+        fb[f] = *reinterpret_cast<const bf16x8*>(sb + (wr * 128 + f * 32 + frag_row) * BK + chunk);
+      }
+    };
 
+    // Prologue: stages 0..2 in flight, wait for stage 0, queue stage 3,
+    // fetch stage 0's first fragments.
+#pragma unroll
+    for (int p = 0; p < NST - 1; ++p) issue_next();
+    stage_sync<2 * DMA_PER_STAGE>();
+    issue_next();
+    bf16x8 fxa[4], fxb[4], fya[4], fyb[4];
+    load_frags(0, 0, fxa, fxb);
+
+    // One stage q: load the second K step's fragments while the first K
+    // step's 16 MFMAs run; mid-stage barrier (stage q+1 landed, everyone is
+    // done with stage q); queue stage q+4 into stage q's slot and load stage
+    // q+1's first fragments while the second K step's 16 MFMAs run.  The
+    // sched_group_barrier pattern spreads the fragment loads and DMAs
+    // between the MFMAs, so the matrix pipe never waits on a burst of memory
+    // instructions.  FIRST = first stage of a vocabulary tile: its first
+    // MFMAs take an inline zero accumulator instead of acc, so acc is never
+    // explicitly cleared (explicit clears get hoisted above the epilogue's
+    // reads and force the accumulators out of AGPRs).
+    f32x16 acc[4][4];
+    const f32x16 zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     int q = 0;
-    for (int vt = vt_lo; vt < vt_hi; ++vt) {
-      f32x16 acc[4][4];
+    auto stage = [&](auto first_tag) {
+      constexpr bool FIRST = decltype(first_tag)::value;
+      load_frags(q & (NST - 1), 1, fya, fyb);
 #pragma unroll
       for (int fv = 0; fv < 4; ++fv)
 #pragma unroll
         for (int fr = 0; fr < 4; ++fr)
+          acc[fv][fr] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fxa[fv], fxb[fr], FIRST ? zero16 : acc[fv][fr], 0,
+                                                                0, 0);
 #pragma unroll
-          for (int x = 0; x < 16; ++x) acc[fv][fr][x] = 0.f;
-
-      for (int ks = 0; ks < KT; ++ks, ++q) {
-        const int ahead = issued - 1 - q;  // stages after q already in flight (0..2)
-        if (ahead >= 2)
-          stage_sync<2 * DMA_PER_STAGE>();
-        else if (ahead == 1)
-          stage_sync<DMA_PER_STAGE>();
-        else
-          stage_sync<0>();
-        // Every wave has finished reading stage q-1: its slot takes the next stage.
-        if (issued < total) issue_next();
-
-        const uint16_t* sa = &lds[q & (NST - 1)][0][0];
-        const uint16_t* sb = &lds[q & (NST - 1)][1][0];
-#pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
-          const int chunk = ((kk * 2 + frag_half) ^ frag_swz) * 8;
-          bf16x8 fa[4], fb[4];
-#pragma unroll
-          for (int f = 0; f < 4; ++f) {
-            fa[f] = *reinterpret_cast<const bf16x8*>(sa + (wv * 128 + f * 32 + frag_row) * BK + chunk);
-            fb[f] = *reinterpret_cast<const bf16x8*>(sb + (wr * 128 + f * 32 + frag_row) * BK + chunk);
-          }
-#pragma unroll
-          for (int fv = 0; fv < 4; ++fv)
-#pragma unroll
-            for (int fr = 0; fr < 4; ++fr)
-              acc[fv][fr] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[fv], fb[fr], acc[fv][fr], 0, 0, 0);
-        }
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
       }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      stage_sync<2 * DMA_PER_STAGE>();
+      issue_next();
+      load_frags((q + 1) & (NST - 1), 0, fxa, fxb);
+#pragma unroll
+      for (int fv = 0; fv < 4; ++fv)
+#pragma unroll
+        for (int fr = 0; fr < 4; ++fr)
+          acc[fv][fr] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fya[fv], fyb[fr], acc[fv][fr], 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // VMEM (DMA)
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      }
+      ++q;
+    };
+    for (int vt = vt_lo; vt < vt_hi; ++vt) {
+      stage(std::true_type{});
+      for (int ks = 1; ks < KT; ++ks) stage(std::false_type{});
 
-      // Online reduction of the finished vocabulary tile.  Accumulator x of
-      // block (fv, fr) is vocabulary entry v0 + fv*32 + 8*(x/4) + x%4 of row
-      // wr*128 + fr*32 + lane%32, with v0 = tile base + wv*128 + 4*(lane/32);
-      // for a fixed lane the index grows with (fv, x), so a strict '>' scan
-      // keeps the lowest index among equal maxima.
+      // Online reduction of the finished vocabulary tile, one 16-value block
+      // at a time.  Accumulator x of block (fv, fr) is vocabulary entry
+      // v0 + fv*32 + 8*(x/4) + x%4 of row wr*128 + fr*32 + lane%32, with
+      // v0 = tile base + wv*128 + 4*(lane/32).  Within a lane the index grows
+      // with (fv, x); strict '>' comparisons in that order keep the lowest
+      // index among equal maxima.
+      // The accumulators are read with explicit v_accvgpr_read (inline asm):
+      // left to itself the register allocator copies all 256 of them to
+      // VGPRs at once and spills.  The compiler does not see these reads as
+      // consumers of the MFMA results for hazard purposes, so 24 wait states
+      // are inserted first, ordered after every MFMA by taking all
+      // accumulators as operands.
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::"a"(acc[0][0]), "a"(acc[0][1]), "a"(acc[0][2]),
+                   "a"(acc[0][3]), "a"(acc[1][0]), "a"(acc[1][1]), "a"(acc[1][2]), "a"(acc[1][3]), "a"(acc[2][0]),
+                   "a"(acc[2][1]), "a"(acc[2][2]), "a"(acc[2][3]), "a"(acc[3][0]), "a"(acc[3][1]), "a"(acc[3][2]),
+                   "a"(acc[3][3]));
       const int v0 = vt * BN + wv * 128 + 4 * frag_half;
       const bool full = (vt + 1) * BN <= V;
 #pragma unroll
       for (int fr = 0; fr < 4; ++fr) {
-        float tm = -INFINITY;
-        int ta = 0;
 #pragma unroll
-        for (int fv = 0; fv < 4; ++fv)
-#pragma unroll
-          for (int x = 0; x < 16; ++x) {
-            const int v = v0 + fv * 32 + 8 * (x >> 2) + (x & 3);
-            const float z = (full || v < V) ? acc[fv][fr][x] : -INFINITY;
-            ta = z > tm ? v : ta;
-            tm = fmaxf(tm, z);
-          }
-        const float mn = fmaxf(run_m[fr], tm);
-        const float sc = (mn == -INFINITY) ? 0.f : mn * kLog2e;
-        float sum = 0.f;
-#pragma unroll
-        for (int fv = 0; fv < 4; ++fv)
+        for (int fv = 0; fv < 4; ++fv) {
+          float z[16];
 #pragma unroll
           for (int x = 0; x < 16; ++x) {
-            const int v = v0 + fv * 32 + 8 * (x >> 2) + (x & 3);
-            const float z = (full || v < V) ? acc[fv][fr][x] : -INFINITY;
-            sum += __builtin_amdgcn_exp2f(fmaf(z, kLog2e, -sc));
+            asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(z[x]) : "a"(acc[fv][fr][x]));
+            if (!full && v0 + fv * 32 + 8 * (x >> 2) + (x & 3) >= V) z[x] = -INFINITY;
           }
-        const float old = (run_m[fr] == -INFINITY) ? 0.f : run_s[fr] * __builtin_amdgcn_exp2f(run_m[fr] * kLog2e - sc);
-        run_s[fr] = old + sum;
-        run_a[fr] = (tm > run_m[fr]) ? ta : run_a[fr];
-        run_m[fr] = mn;
+          float bm = z[0];
+          int bi = 0;
+#pragma unroll
+          for (int x = 1; x < 16; ++x) {
+            bi = z[x] > bm ? (8 * (x >> 2) + (x & 3)) : bi;
+            bm = fmaxf(bm, z[x]);
+          }
+          const float mn = fmaxf(run_m[fr], bm);
+          if (mn != -INFINITY) {
+            const float sc = mn * kLog2e;
+            float sum = 0.f;
+#pragma unroll
+            for (int x = 0; x < 16; ++x) sum += __builtin_amdgcn_exp2f(fmaf(z[x], kLog2e, -sc));
+            const float old = (run_m[fr] == -INFINITY) ? 0.f : run_s[fr] * __builtin_amdgcn_exp2f(fmaf(run_m[fr], kLog2e, -sc));
+            run_s[fr] = old + sum;
+            run_a[fr] = (bm > run_m[fr]) ? v0 + fv * 32 + bi : run_a[fr];
+            run_m[fr] = mn;
+          }
+        }
       }
     }
 
