@@ -137,7 +137,7 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_persistent(const uint16_t* __res
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS DMA addresses stay scalar
   const int wr = wave >> 1;   // rows [wr * 128, +128)
   const int wv = wave & 1;    // vocabulary [wv * 128, +128)
 
@@ -187,32 +187,36 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_persistent(const uint16_t* __res
     // with the MFMAs) and always has two stages in flight behind the one it
     // waits for.  The item's final vmcnt(0) drains the extra DMAs.
     int iss_vt = vt_lo, iss_k0 = 0, iss_slot = 0;
-    auto issue_next = [&]() {
-      uint16_t* sa = &lds[iss_slot][0][0] + wave * DMA_ROWS * BK;
-      uint16_t* sb = &lds[iss_slot][1][0] + wave * DMA_ROWS * BK;
-      // Rows past V (last vocabulary tile only) re-read row 0 of the tile;
-      // the epilogue drops their logits.
-      const int vbase = (iss_vt < vt_hi ? iss_vt : vt_hi - 1) * BN;
-      const char* Wb = reinterpret_cast<const char*>(W + (size_t)vbase * (size_t)d + iss_k0);
-      const bool wfull = vbase + BN <= V;
-#pragma unroll
-      for (int i = 0; i < DMA_PER_OPERAND; ++i) {
-        const uint32_t o = (wfull || vbase + (wave + 4 * i) * DMA_ROWS + dma_row < V) ? woff[i]
-                                                                                       : (uint32_t)(dma_chunk * 16);
-        __builtin_amdgcn_global_load_lds((const void*)(Wb + o), (LDS_AS void*)(sa + i * 4 * DMA_ROWS * BK), 16, 0,
-                                         0);
+    // DMA i of the next stage: i < 4 -> W_lm rows block wave + 4 i, else
+    // hidden rows block wave + 4 (i - 4).  Rows past V (last vocabulary tile
+    // only) re-read row 0 of the tile; the epilogue drops their logits.
+    auto issue_dma = [&](int i) {
+      if (i < DMA_PER_OPERAND) {
+        uint16_t* sa = &lds[iss_slot][0][0] + (wave + 4 * i) * DMA_ROWS * BK;
+        const int vbase = (iss_vt < vt_hi ? iss_vt : vt_hi - 1) * BN;
+        const char* Wb = reinterpret_cast<const char*>(W + (size_t)vbase * (size_t)d + iss_k0);
+        const bool keep = vbase + BN <= V || vbase + (wave + 4 * i) * DMA_ROWS + dma_row < V;
+        const uint32_t o = keep ? woff[i] : (uint32_t)(dma_chunk * 16);
+        __builtin_amdgcn_global_load_lds((const void*)(Wb + o), (LDS_AS void*)sa, 16, 0, 0);
+      } else {
+        const int j = i - DMA_PER_OPERAND;
+        uint16_t* sb = &lds[iss_slot][1][0] + (wave + 4 * j) * DMA_ROWS * BK;
+        const char* Hk = Hb + (size_t)iss_k0 * 2u;
+        __builtin_amdgcn_global_load_lds((const void*)(Hk + hoff[j]), (LDS_AS void*)sb, 16, 0, 0);
       }
-      const char* Hk = Hb + (size_t)iss_k0 * 2u;
-#pragma unroll
-      for (int i = 0; i < DMA_PER_OPERAND; ++i)
-        __builtin_amdgcn_global_load_lds((const void*)(Hk + hoff[i]), (LDS_AS void*)(sb + i * 4 * DMA_ROWS * BK),
-                                         16, 0, 0);
+    };
+    auto advance_issue = [&]() {
       iss_slot = (iss_slot + 1) & (NST - 1);
       iss_k0 += BK;
       if (iss_k0 == d) {
         iss_k0 = 0;
         ++iss_vt;
       }
+    };
+    auto issue_next = [&]() {
+#pragma unroll
+      for (int i = 0; i < DMA_PER_STAGE; ++i) issue_dma(i);
+      advance_issue();
     };
 
     float run_m[4], run_s[4];
@@ -224,16 +228,20 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_persistent(const uint16_t* __res
       run_a[fr] = 0;
     }
 
-    // Fragment loads of K step kk (0/1) of ring slot `slot`.
-    auto load_frags = [&](int slot, int kk, bf16x8* fa, bf16x8* fb) {
-      const uint16_t* sa = &lds[slot][0][0];
-      const uint16_t* sb = &lds[slot][1][0];
+    // Fragment loads of K step kk (0/1) of ring slot `slot`: fragment i
+    // (i = 0..7) is W_lm block i/2 when i is even, hidden block i/2 when odd,
+    // so the first MFMA's operands arrive first.
+    auto load_frag = [&](int slot, int kk, int i, bf16x8* fa, bf16x8* fb) {
       const int chunk = ((kk * 2 + frag_half) ^ frag_swz) * 8;
+      const int f = i >> 1;
+      if ((i & 1) == 0)
+        fa[f] = *reinterpret_cast<const bf16x8*>(&lds[slot][0][0] + (wv * 128 + f * 32 + frag_row) * BK + chunk);
+      else
+        fb[f] = *reinterpret_cast<const bf16x8*>(&lds[slot][1][0] + (wr * 128 + f * 32 + frag_row) * BK + chunk);
+    };
+    auto load_frags = [&](int slot, int kk, bf16x8* fa, bf16x8* fb) {
 #pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        fa[f] = *reinterpret_cast<const bf16x8*>(sa + (wv * 128 + f * 32 + frag_row) * BK + chunk);
-        fb[f] = *reinterpret_cast<const bf16x8*>(sb + (wr * 128 + f * 32 + frag_row) * BK + chunk);
-      }
+      for (int i = 0; i < 8; ++i) load_frag(slot, kk, i, fa, fb);
     };
 
     // Prologue: stages 0..2 in flight, wait for stage 0, queue stage 3,
@@ -260,34 +268,34 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_persistent(const uint16_t* __res
     int q = 0;
     auto stage = [&](auto first_tag) {
       constexpr bool FIRST = decltype(first_tag)::value;
-      load_frags(q & (NST - 1), 1, fya, fyb);
+      // First K step: MFMA pair m (blocks 2m, 2m+1), then the second K
+      // step's fragment m.  sched_barrier fixes the interleave.
 #pragma unroll
-      for (int fv = 0; fv < 4; ++fv)
+      for (int m = 0; m < 8; ++m) {
 #pragma unroll
-        for (int fr = 0; fr < 4; ++fr)
+        for (int t = 0; t < 2; ++t) {
+          const int fv = (2 * m + t) >> 2, fr = (2 * m + t) & 3;
           acc[fv][fr] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fxa[fv], fxb[fr], FIRST ? zero16 : acc[fv][fr], 0,
                                                                 0, 0);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+        }
+        load_frag(q & (NST - 1), 1, m, fya, fyb);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
       stage_sync<2 * DMA_PER_STAGE>();
-      issue_next();
-      load_frags((q + 1) & (NST - 1), 0, fxa, fxb);
+      // Second K step: MFMA pair m, DMA m of stage q+4 (into stage q's
+      // slot), fragment m of stage q+1's first K step.
 #pragma unroll
-      for (int fv = 0; fv < 4; ++fv)
+      for (int m = 0; m < 8; ++m) {
 #pragma unroll
-        for (int fr = 0; fr < 4; ++fr)
+        for (int t = 0; t < 2; ++t) {
+          const int fv = (2 * m + t) >> 2, fr = (2 * m + t) & 3;
           acc[fv][fr] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fya[fv], fyb[fr], acc[fv][fr], 0, 0, 0);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // VMEM (DMA)
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+        }
+        issue_dma(m);
+        load_frag((q + 1) & (NST - 1), 0, m, fxa, fxb);
+        __builtin_amdgcn_sched_barrier(0);
       }
+      advance_issue();
       ++q;
     };
     for (int vt = vt_lo; vt < vt_hi; ++vt) {
