@@ -175,7 +175,81 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_scatter(
   }
 }
 
+// Few rows (<= kSmallBM, the semi-autoregressive block): one workgroup
+// merges every row's slices (a wave per row, lanes across slices, then a
+// butterfly), ranks the rows by counting (row r precedes r' iff its
+// confidence is larger, or equal with the lower row = lower position) and
+// commits the first n = min(k, M).
+constexpr int kFinishThreads = 1024;
+__global__ __launch_bounds__(kFinishThreads) void k_finish_small(const int32_t* __restrict__ ctr,
+                                                                const int32_t* __restrict__ idx,
+                                                                const float* __restrict__ pm,
+                                                                const int32_t* __restrict__ pa,
+                                                                const float* __restrict__ ps, int k,
+                                                                uint8_t* __restrict__ mask,
+                                                                int32_t* __restrict__ tokens, dllm_step_out o) {
+  __shared__ float s_conf[kSmallBM], s_lse[kSmallBM];
+  __shared__ int s_tok[kSmallBM];
+  const int M = ctr[0];
+  const int slices = ctr[3];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int r = wave; r < M; r += kFinishThreads / 64) {
+    const size_t base = (size_t)r * (size_t)slices;
+    float m = -INFINITY, s = 0.f;
+    int a = 0x7FFFFFFF;
+    for (int j = lane; j < slices; j += 64) merge_state(m, a, s, pm[base + j], pa[base + j], ps[base + j]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float m2 = __shfl_xor(m, off);
+      const int a2 = __shfl_xor(a, off);
+      const float s2 = __shfl_xor(s, off);
+      merge_state(m, a, s, m2, a2, s2);
+    }
+    if (lane == 0) {
+      s_conf[r] = 1.0f / s;
+      s_lse[r] = m + __builtin_amdgcn_logf(s) * kLn2;
+      s_tok[r] = a;
+    }
+  }
+  __syncthreads();
+  const int n = k < M ? k : M;
+  const int t = threadIdx.x;
+  if (t < M) {
+    const float c = s_conf[t];
+    int rank = 0;
+    for (int r2 = 0; r2 < M; ++r2) {
+      const float c2 = s_conf[r2];
+      rank += (c2 > c || (c2 == c && r2 < t)) ? 1 : 0;
+    }
+    const int pos = idx[t];
+    const int tok = s_tok[t];
+    if (o.row_idx) o.row_idx[t] = pos;
+    if (o.row_tok) o.row_tok[t] = tok;
+    if (o.row_conf) o.row_conf[t] = c;
+    if (o.row_lse) o.row_lse[t] = s_lse[t];
+    if (rank < n) {
+      tokens[pos] = tok;
+      mask[pos] = 0;
+      if (o.sel_idx) o.sel_idx[rank] = pos;
+      if (o.sel_tok) o.sel_tok[rank] = tok;
+      if (o.sel_conf) o.sel_conf[rank] = c;
+    }
+  }
+  if (t == 0) {
+    if (o.n_out) *o.n_out = n;
+    if (o.m_out) *o.m_out = M;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_finish_small(const int32_t* ctr, const int32_t* idx, const float* pm, const int32_t* pa,
+                               const float* ps, int k, uint8_t* mask, int32_t* tokens, dllm_step_out out,
+                               hipStream_t stream) {
+  hipLaunchKernelGGL(k_finish_small, dim3(1), dim3(kFinishThreads), 0, stream, ctr, idx, pm, pa, ps, k, mask, tokens,
+                     out);
+  return hipGetLastError();
+}
 
 hipError_t launch_merge(const int32_t* ctr, const int32_t* idx, const float* pm, const int32_t* pa,
                         const float* ps, int max_rows, int32_t* row_tok, float* row_conf,

@@ -221,6 +221,12 @@ dllm_status dllm_masked_readout_step(dllm_readout* h, const uint16_t* hidden, in
               h->cus);
     if (e != hipSuccess) return DLLM_ERR_HIP;
     if (h->ev_after && hipEventRecord(h->ev_after, st) != hipSuccess) return DLLM_ERR_HIP;
+    if (path == kSmall) {
+      // merge, selection and commit of <= 32 rows in one workgroup
+      if (dllm::launch_finish_small(w.ctr, w.idx, w.part_m, w.part_a, w.part_s, k, mask, tokens, o, st) != hipSuccess)
+        return DLLM_ERR_HIP;
+      return DLLM_OK;
+    }
     if (dllm::launch_merge(w.ctr, w.idx, w.part_m, w.part_a, w.part_s, (int)rows_max, w.row_tok,
                            w.row_conf, w.row_lse, w.keys, o.row_idx, o.row_tok, o.row_conf, o.row_lse,
                            st) != hipSuccess)

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "dllm_readout.h"
+
 namespace dllm {
 
 // Layout of the device workspace, carved by the host at create time.
@@ -62,6 +64,12 @@ hipError_t launch_gemm_persistent(const uint16_t* W, const uint16_t* H, int d, i
 hipError_t launch_gemm_small(const uint16_t* W, const uint16_t* H, int d, int V, const int32_t* idx,
                              const int32_t* ctr, int slices, float* pm, int32_t* pa, float* ps,
                              hipStream_t stream);
+
+// Merge + selection + commit for at most kSmallBM candidate rows, in one
+// workgroup (replaces launch_merge + launch_topk_scatter on the small path).
+hipError_t launch_finish_small(const int32_t* ctr, const int32_t* idx, const float* pm, const int32_t* pa,
+                               const float* ps, int k, uint8_t* mask, int32_t* tokens, dllm_step_out out,
+                               hipStream_t stream);
 
 hipError_t launch_merge(const int32_t* ctr, const int32_t* idx, const float* pm, const int32_t* pa,
                         const float* ps, int max_rows, int32_t* row_tok, float* row_conf,
