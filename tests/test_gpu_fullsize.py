@@ -28,7 +28,7 @@ def _readout(Wt, L_max, k_max):
 
 
 def test_llada_semi_ar_32_steps():
-    cfg = WL.CONFIGS[2]
+    cfg = WL.WORKLOADS["llada_like_semi_ar"]
     W = WL.w_lm(cfg)
     W64 = oracle.widen_bf16(W)
     mask, tokens = WL.initial_state(cfg)
@@ -56,10 +56,10 @@ def test_llada_semi_ar_32_steps():
     print(f"llada: near-tie rows {total_ties}, band rows {total_band}")
 
 
-def _sampled_case(cid, n_random=384, n_boundary=256):
+def _sampled_case(name, n_random=384, n_boundary=256):
     import torch
-    cfg = WL.CONFIGS[cid]
-    print(f"[case] full-size config {cid} {cfg.name}: generating", flush=True)
+    cfg = WL.WORKLOADS[name]
+    print(f"[case] full-size {name}: generating", flush=True)
     inp = WL.make(cfg)
     Wt, Ht, mt, tt = to_dev(inp.W, inp.H, inp.mask, inp.tokens)
     rd = _readout(Wt, cfg.L, cfg.k)
@@ -78,7 +78,7 @@ def _sampled_case(cid, n_random=384, n_boundary=256):
     np.testing.assert_array_equal(g["sel_conf"], g["row_conf"][keys[:n]])
 
     # (2) oracle rows: committed, just below the boundary, and a random sample
-    rng = np.random.default_rng(1000 + cid)
+    rng = np.random.default_rng(1000 + cfg.id)
     if n < M:
         # every row whose library confidence could, within the tolerances, still
         # reach the oracle's boundary (with a safety factor), at least n_boundary
@@ -89,9 +89,9 @@ def _sampled_case(cid, n_random=384, n_boundary=256):
     boundary = keys[n:n + n_boundary]
     sample = rng.choice(M, size=min(n_random, M), replace=False)
     rows = np.unique(np.concatenate([keys[:n], boundary, sample]))
-    print(f"[case] config {cid}: oracle on {len(rows)} rows", flush=True)
+    print(f"[case] {name}: oracle on {len(rows)} rows", flush=True)
     st = oracle.readout_rows(inp.H, inp.W, g["row_idx"][rows])
-    ties = check_rows(g["row_tok"][rows], g["row_conf"][rows], g["row_lse"][rows], st, f"config {cid}")
+    ties = check_rows(g["row_tok"][rows], g["row_conf"][rows], g["row_lse"][rows], st, f"{name}")
 
     # (3) no unchecked row can reach the oracle's top n: every unchecked row has a
     # library confidence at or below the last boundary row's, and the sampled
@@ -100,23 +100,23 @@ def _sampled_case(cid, n_random=384, n_boundary=256):
         c_edge = float(g["row_conf"][keys[n + n_boundary - 1]])
         c_min_sel = float(st["conf"][np.searchsorted(rows, keys[:n])].min())
         assert c_edge / (1 - REL) < c_min_sel * np.exp(-GAP), \
-            f"config {cid}: boundary set too small to exclude unchecked rows"
-    band = check_selection(g["sel_idx"], g["row_idx"][rows], st["logconf"], n, f"config {cid}")
-    check_rank_order(g["sel_idx"], g["row_idx"][rows], st["logconf"], f"config {cid}")
-    print(f"config {cid}: M={M} n={n} checked rows={len(rows)} near-tie rows={ties} band rows={band}")
+            f"{name}: boundary set too small to exclude unchecked rows"
+    band = check_selection(g["sel_idx"], g["row_idx"][rows], st["logconf"], n, f"{name}")
+    check_rank_order(g["sel_idx"], g["row_idx"][rows], st["logconf"], f"{name}")
+    print(f"{name}: M={M} n={n} checked rows={len(rows)} near-tie rows={ties} band rows={band}")
     return inp, g
 
 
 def test_dream_like_sampled():
-    _sampled_case(3)
+    _sampled_case("dream_like")
 
 
 def test_long_context_low_mask_sampled():
-    _sampled_case(4)
+    _sampled_case("long_ctx_low_mask")
 
 
 def test_long_context_high_mask_planted():
-    inp, g = _sampled_case(5)
+    inp, g = _sampled_case("long_ctx_high_mask")
     P = inp.plant
     planted = dict(zip(P.rows.tolist(), P.tokens.tolist()))
     # independent of the oracle: committed rows are planted rows with their planted token

@@ -51,7 +51,7 @@ def _parity_case(H, W, mask, tokens, k, lo=0, hi=None, block=0, rd=None, slices=
 
 
 def test_tiny_config_parity():
-    inp = WL.make(1)
+    inp = WL.make("tiny")
     cfg = inp.cfg
     g, o, ties, band = _parity_case(inp.H, inp.W, inp.mask, inp.tokens, cfg.k, where="tiny")
     assert g["M"] == int(inp.mask.sum()) and g["n"] == cfg.k

@@ -389,7 +389,7 @@ def test_planted_rows_give_planted_tokens():
     """A small copy of the high-mask long-context workload: the generator's
     plant record (not the oracle) says which token each planted row must
     read out, and planted rows must outrank the rest."""
-    cfg = WL.small_config(WL.CONFIGS[5], L=4096, d=512, V=4096, k=64)
+    cfg = WL.small_config(WL.WORKLOADS["long_ctx_high_mask"], L=4096, d=512, V=4096, k=64)
     inp = WL.make(cfg)
     P = inp.plant
     assert len(P.rows) == round(0.05 * cfg.L)

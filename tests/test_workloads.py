@@ -20,7 +20,7 @@ def test_bf16_round_matches_torch_rne():
 
 
 def test_same_seed_same_bytes_and_thread_independence(monkeypatch):
-    cfg = WL.small_config(WL.CONFIGS[3], L=300, d=64, V=20000, k=8)
+    cfg = WL.small_config(WL.WORKLOADS["dream_like"], L=300, d=64, V=20000, k=8)
     a = WL.w_lm(cfg)
     monkeypatch.setattr(WL, "_threads", lambda: 1)
     b = WL.w_lm(cfg)
@@ -32,9 +32,10 @@ def test_same_seed_same_bytes_and_thread_independence(monkeypatch):
     assert WL.sha256(WL.w_lm(other)) != WL.sha256(a)
 
 
-@pytest.mark.parametrize("cid,M", [(3, 7373), (4, 13107), (5, 117965)])
-def test_documented_mask_counts(cid, M):
-    cfg = WL.CONFIGS[cid]
+@pytest.mark.parametrize("name,M", [("dream_like", 7373), ("long_ctx_low_mask", 13107),
+                                    ("long_ctx_high_mask", 117965)])
+def test_documented_mask_counts(name, M):
+    cfg = WL.WORKLOADS[name]
     mask, tokens = WL.initial_state(cfg)
     assert mask.shape == (cfg.L,) and mask.dtype == np.uint8
     assert int(mask.sum()) == M
@@ -43,15 +44,15 @@ def test_documented_mask_counts(cid, M):
 
 
 def test_tiny_and_semi_ar_masks():
-    m1, _ = WL.initial_state(WL.CONFIGS[1])
+    m1, _ = WL.initial_state(WL.WORKLOADS["tiny"])
     assert 200 < int(m1.sum()) < 312          # Bernoulli(0.5) over 512
-    m2, _ = WL.initial_state(WL.CONFIGS[2])
+    m2, _ = WL.initial_state(WL.WORKLOADS["llada_like_semi_ar"])
     assert m2[:3072].sum() == 0 and m2[3072:].all()
-    assert WL.CONFIGS[2].win == (3072, 4096)
+    assert WL.WORKLOADS["llada_like_semi_ar"].win == (3072, 4096)
 
 
 def test_distributions_and_rms_norm():
-    cfg = WL.small_config(WL.CONFIGS[2], L=64, d=4096, V=512)
+    cfg = WL.small_config(WL.WORKLOADS["llada_like_semi_ar"], L=64, d=4096, V=512)
     H, _ = WL.hidden(cfg, step=3)
     h = WL.bf16_to_f32(H).astype(np.float64)
     rms = np.sqrt((h ** 2).mean(axis=1))
@@ -63,7 +64,7 @@ def test_distributions_and_rms_norm():
 
 
 def test_plant_record():
-    cfg = WL.small_config(WL.CONFIGS[5], L=2000, d=128, V=1000)
+    cfg = WL.small_config(WL.WORKLOADS["long_ctx_high_mask"], L=2000, d=128, V=1000)
     W = WL.w_lm(cfg)
     H, P = WL.hidden(cfg, W)
     assert len(P.rows) == 100 and np.all(np.diff(P.rows) > 0)

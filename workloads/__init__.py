@@ -40,7 +40,7 @@ RMS_EPS = 1e-6           # RMS normalisation of the LLaDA-like hidden states
 
 @dataclass(frozen=True)
 class Config:
-    """One synthetic workload.
+    """One synthetic workload (``id`` only selects its random streams).
 
     ``mask_kind``: "bernoulli" (each position masked with prob ``mask_ratio``),
     "exact" (exactly round(mask_ratio * L) positions, uniform without
@@ -72,18 +72,18 @@ class Config:
         return (0, self.L)
 
 
-CONFIGS: dict[int, Config] = {
-    1: Config(1, "tiny", L=512, d=256, V=4096, k=32,
+WORKLOADS: dict[str, Config] = {c.name: c for c in (
+    Config(1, "tiny", L=512, d=256, V=4096, k=32,
               mask_kind="bernoulli", mask_ratio=0.5),
-    2: Config(2, "llada_like_semi_ar", L=4096, d=4096, V=126464, k=2, steps=32,
+    Config(2, "llada_like_semi_ar", L=4096, d=4096, V=126464, k=2, steps=32,
               mask_kind="suffix", suffix=1024, block=32, rms_norm=True),
-    3: Config(3, "dream_like", L=8192, d=3584, V=152064, k=64,
+    Config(3, "dream_like", L=8192, d=3584, V=152064, k=64,
               mask_kind="exact", mask_ratio=0.9),
-    4: Config(4, "long_ctx_low_mask", L=131072, d=4096, V=126464, k=256,
+    Config(4, "long_ctx_low_mask", L=131072, d=4096, V=126464, k=256,
               mask_kind="exact", mask_ratio=0.1),
-    5: Config(5, "long_ctx_high_mask", L=131072, d=4096, V=126464, k=1024,
-              mask_kind="exact", mask_ratio=0.9, plant_frac=0.05),
-}
+    Config(5, "long_ctx_high_mask", L=131072, d=4096, V=126464, k=1024,
+           mask_kind="exact", mask_ratio=0.9, plant_frac=0.05),
+)}
 
 MASK_TOKEN_OFFSET = 0   # masked positions hold token id V + this (outside the vocabulary)
 
@@ -232,9 +232,9 @@ class StepInputs:
     meta: dict = field(default_factory=dict)
 
 
-def make(cfg_or_id, W_bits: np.ndarray | None = None) -> StepInputs:
-    """All inputs of the first step of a config."""
-    cfg = CONFIGS[cfg_or_id] if isinstance(cfg_or_id, int) else cfg_or_id
+def make(cfg_or_name, W_bits: np.ndarray | None = None) -> StepInputs:
+    """All inputs of the first step of a workload (a Config or its name)."""
+    cfg = WORKLOADS[cfg_or_name] if isinstance(cfg_or_name, str) else cfg_or_name
     W = w_lm(cfg) if W_bits is None else W_bits
     H, plant = hidden(cfg, W, 0)
     mask, tokens = initial_state(cfg)
