@@ -130,7 +130,60 @@ __global__ __launch_bounds__(kThreads) void k_mask_compact(const uint8_t* __rest
   }
 }
 
+// Small candidate windows (the host knows at most 32 rows can come out): one
+// wave, no barriers.  Block search reads 16 bytes per lane per iteration;
+// the candidate block (<= 32 positions) is compacted with one ballot.
+__global__ __launch_bounds__(64) void k_mask_compact_small(const uint8_t* __restrict__ mask, int64_t win_lo,
+                                                          int64_t win_hi, int64_t block, int fixed_slices,
+                                                          int32_t* __restrict__ idx, int32_t* __restrict__ ctr) {
+  const int lane = threadIdx.x;
+  int lo = (int)win_lo, hi = (int)win_hi;
+  if (block > 0) {
+    int first = hi;
+    for (int base = lo; base < hi; base += 64 * 16) {
+      int mine = hi;
+      const int p0 = base + lane * 16;
+#pragma unroll
+      for (int j = 15; j >= 0; --j) {
+        const int p = p0 + j;
+        if (p < hi && mask[p] != 0) mine = p;
+      }
+      // lowest position over the wave: lanes cover increasing positions
+      const unsigned long long bal = __ballot(mine < hi);
+      if (bal) {
+        first = __shfl(mine, __ffsll((long long)bal) - 1);
+        break;
+      }
+    }
+    if (first >= hi) {
+      lo = hi;
+    } else {
+      const int64_t blo = win_lo + (int64_t)((first - lo) / block) * block;
+      const int64_t bhi = blo + block < (int64_t)hi ? blo + block : (int64_t)hi;
+      lo = (int)blo;
+      hi = (int)bhi;
+    }
+  }
+  const bool cand = lane < hi - lo && mask[lo + lane] != 0;  // hi - lo <= 32 here
+  const unsigned long long bal = __ballot(cand);
+  if (cand) idx[__popcll(bal & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))))] = lo + lane;
+  if (lane == 0) {
+    ctr[0] = __popcll(bal);
+    ctr[1] = lo;
+    ctr[2] = hi;
+    ctr[3] = fixed_slices;
+    ctr[4] = 1;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_mask_compact_small(const uint8_t* mask, int64_t win_lo, int64_t win_hi, int64_t block,
+                                     int fixed_slices, int32_t* idx, int32_t* ctr, hipStream_t stream) {
+  hipLaunchKernelGGL(k_mask_compact_small, dim3(1), dim3(64), 0, stream, mask, win_lo, win_hi, block, fixed_slices,
+                     idx, ctr);
+  return hipGetLastError();
+}
 
 hipError_t launch_mask_compact(const uint8_t* mask, int64_t win_lo, int64_t win_hi, int64_t block,
                                PlanParams plan, int32_t* idx, int32_t* ctr, hipStream_t stream) {

@@ -176,11 +176,13 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_scatter(
 }
 
 // Few rows (<= kSmallBM, the semi-autoregressive block): one workgroup
-// merges every row's slices (a wave per row, lanes across slices, then a
-// butterfly), ranks the rows by counting (row r precedes r' iff its
-// confidence is larger, or equal with the lower row = lower position) and
-// commits the first n = min(k, M).
+// merges every row's slices (16-byte (m, a, s, 0) records written by the
+// streaming GEMM into pm; 32 lanes per row, loads issued 16 at a time
+// so their latencies overlap, then a butterfly), ranks the rows by counting
+// (row r precedes r' iff its confidence is larger, or equal with the lower
+// row = lower position) and commits the first n = min(k, M).
 constexpr int kFinishThreads = 1024;
+static_assert(kFinishThreads == 32 * kSmallBM, "32 lanes per row");
 __global__ __launch_bounds__(kFinishThreads) void k_finish_small(const int32_t* __restrict__ ctr,
                                                                 const int32_t* __restrict__ idx,
                                                                 const float* __restrict__ pm,
@@ -192,20 +194,35 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish_small(const int32_t* 
   __shared__ int s_tok[kSmallBM];
   const int M = ctr[0];
   const int slices = ctr[3];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int r = wave; r < M; r += kFinishThreads / 64) {
+  const int r = threadIdx.x >> 5, sub = threadIdx.x & 31;
+  if (r < M) {
     const size_t base = (size_t)r * (size_t)slices;
     float m = -INFINITY, s = 0.f;
     int a = 0x7FFFFFFF;
-    for (int j = lane; j < slices; j += 64) merge_state(m, a, s, pm[base + j], pa[base + j], ps[base + j]);
+    constexpr int U = 16;
+    for (int j0 = sub; j0 < slices; j0 += 32 * U) {
+      float mu[U], su[U];
+      int au[U];
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
+      for (int u = 0; u < U; ++u) {
+        const int j = j0 + 32 * u;
+        float4 rec = make_float4(-INFINITY, __int_as_float(0x7FFFFFFF), 0.f, 0.f);
+        if (j < slices) rec = reinterpret_cast<const float4*>(pm)[base + j];
+        mu[u] = rec.x;
+        au[u] = __float_as_int(rec.y);
+        su[u] = rec.z;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) merge_state(m, a, s, mu[u], au[u], su[u]);
+    }
+#pragma unroll
+    for (int off = 16; off >= 1; off >>= 1) {  // within the 32-lane half of the wave
       const float m2 = __shfl_xor(m, off);
       const int a2 = __shfl_xor(a, off);
       const float s2 = __shfl_xor(s, off);
       merge_state(m, a, s, m2, a2, s2);
     }
-    if (lane == 0) {
+    if (sub == 0) {
       s_conf[r] = 1.0f / s;
       s_lse[r] = m + __builtin_amdgcn_logf(s) * kLn2;
       s_tok[r] = a;

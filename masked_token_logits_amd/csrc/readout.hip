@@ -41,7 +41,8 @@ size_t carve(int64_t L_max, int64_t V, uint8_t* base, dllm::Workspace* ws) {
   // whole 256-row tiles times the largest slice count, so any plan with S <= 64 fits
   const int64_t part_cap_large = (L_max + dllm::kLargeBM - 1) / dllm::kLargeBM * dllm::kLargeBM *
                                  dllm::kMaxLargeSlices;
-  const int64_t part_cap_small = (int64_t)dllm::kSmallBM * small_slice_count(V);
+  // the few-row path stores 16-byte (m, a, s, 0) records in part_m: 4 floats per partial
+  const int64_t part_cap_small = 4 * (int64_t)dllm::kSmallBM * small_slice_count(V);
   const int64_t part_cap = part_cap_large > part_cap_small ? part_cap_large : part_cap_small;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -199,8 +200,11 @@ dllm_status dllm_masked_readout_step(dllm_readout* h, const uint16_t* hidden, in
     plan.fixed_slices = sl;
     plan.tile_rows = dllm::kLargeBM;
   }
-  if (dllm::launch_mask_compact(mask, win_lo, win_hi, block, plan, w.idx, w.ctr, st) != hipSuccess)
-    return DLLM_ERR_HIP;
+  const hipError_t ce = (path == kSmall)
+                            ? dllm::launch_mask_compact_small(mask, win_lo, win_hi, block, plan.fixed_slices, w.idx,
+                                                              w.ctr, st)
+                            : dllm::launch_mask_compact(mask, win_lo, win_hi, block, plan, w.idx, w.ctr, st);
+  if (ce != hipSuccess) return DLLM_ERR_HIP;
 
   if (rows_max > 0) {
     hipError_t e;

@@ -50,6 +50,10 @@ struct PlanParams {
 hipError_t launch_mask_compact(const uint8_t* mask, int64_t win_lo, int64_t win_hi, int64_t block,
                                PlanParams plan, int32_t* idx, int32_t* ctr, hipStream_t stream);
 
+// The same for windows that hold at most 32 candidates (one wave).
+hipError_t launch_mask_compact_small(const uint8_t* mask, int64_t win_lo, int64_t win_hi, int64_t block,
+                                     int fixed_slices, int32_t* idx, int32_t* ctr, hipStream_t stream);
+
 hipError_t launch_gemm_large(const uint16_t* W, const uint16_t* H, int d, int V, const int32_t* idx,
                              const int32_t* ctr, int n_row_tiles, int slices, float* pm, int32_t* pa,
                              float* ps, hipStream_t stream);
