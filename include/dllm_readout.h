@@ -65,9 +65,10 @@ typedef enum {
  * Optional per-step outputs (host struct of device pointers; each may be
  * NULL).  "Rows" are the candidate positions of the step in ascending
  * position order; there are M of them (M <= the window length).
- *   n_out     [1]      n = min(k, M), the number of committed positions
+ *   n_out     [1]      n, the number of committed positions (min(k, M) for
+ *                      top-k; the threshold rule of dllm_policy otherwise)
  *   m_out     [1]      M
- *   sel_idx   [k_max]  committed positions in rank order (confidence
+ *   sel_idx   [k_max]  committed positions in rank order (score
  *                      descending, position ascending); first n valid
  *   sel_tok   [k_max]  their tokens
  *   sel_conf  [k_max]  their confidences (float32)
@@ -75,6 +76,13 @@ typedef enum {
  *   row_tok   [L_max]  argmax token of each candidate row
  *   row_conf  [L_max]  confidence = max softmax probability = exp(max - lse)
  *   row_lse   [L_max]  natural log-sum-exp of the row's logits
+ *   row_margin  [L_max]  largest minus second-largest softmax probability
+ *                        (0 when the largest logit repeats)
+ *   row_entropy [L_max]  -sum_v p_v ln p_v of the row's softmax
+ * Asking for row_margin or row_entropy (or ranking by them, dllm_policy)
+ * makes the GEMM keep two more running values per row, in the same pass.
+ * "Rank order" is by the step's ranking score (dllm_policy); sel_conf always
+ * holds confidences.
  */
 typedef struct {
   int32_t *n_out;
@@ -86,7 +94,38 @@ typedef struct {
   int32_t *row_tok;
   float *row_conf;
   float *row_lse;
+  float *row_margin;
+  float *row_entropy;
 } dllm_step_out;
+
+/*
+ * Ranking score of a candidate row (the unmasking policies the survey
+ * groups as confidence- and entropy-driven: Accelerating Masked Diffusion
+ * Large Language Models: A Survey of Efficient Inference Techniques, Main
+ * Findings).  Larger scores commit first.
+ */
+typedef enum {
+  DLLM_SCORE_CONF = 0,       /* largest softmax probability */
+  DLLM_SCORE_MARGIN = 1,     /* largest minus second-largest probability */
+  DLLM_SCORE_NEG_ENTROPY = 2 /* minus the softmax entropy (nats) */
+} dllm_score;
+
+/*
+ * Selection policy of a step.
+ *   score          a dllm_score
+ *   use_threshold  0: commit the n = min(k, M) best rows (top-k).
+ *                  1: adaptive parallel decoding (Dynamic-dLLM, abstract):
+ *                  commit every row whose score is >= tau, but at least one
+ *                  (the best) and at most k: n = min(max(#{score >= tau}, 1),
+ *                  k, M); n = 0 when M = 0 or k = 0.  The comparison is
+ *                  made in float32 on the float32 score.
+ *   tau            threshold (ignored for top-k); must not be NaN
+ */
+typedef struct {
+  int32_t score;
+  int32_t use_threshold;
+  float tau;
+} dllm_policy;
 
 /*
  * Bytes of device workspace a handle needs for these limits (host-only
@@ -134,6 +173,18 @@ dllm_status dllm_masked_readout_create(dllm_readout **out, const uint16_t *W_lm,
 dllm_status dllm_masked_readout_step(dllm_readout *h, const uint16_t *hidden, int64_t L,
                                      uint8_t *mask, int32_t *tokens, int32_t k, int64_t win_lo,
                                      int64_t win_hi, int64_t block, const dllm_step_out *out);
+
+/*
+ * One readout step under a selection policy (NULL = top-k by confidence,
+ * which is exactly dllm_masked_readout_step).  Arguments as for
+ * dllm_masked_readout_step; ties in the score commit the lower position
+ * first.  DLLM_ERR_INVALID_ARG for an unknown score, use_threshold not 0 or
+ * 1, or a NaN tau.
+ */
+dllm_status dllm_masked_readout_step_ex(dllm_readout *h, const uint16_t *hidden, int64_t L,
+                                        uint8_t *mask, int32_t *tokens, int32_t k, int64_t win_lo,
+                                        int64_t win_hi, int64_t block, const dllm_policy *policy,
+                                        const dllm_step_out *out);
 
 /* Free the host handle (no device memory is owned).  NULL -> DLLM_OK. */
 dllm_status dllm_masked_readout_destroy(dllm_readout *h);

@@ -3,7 +3,8 @@
 One step gathers the hidden states of still-masked positions, projects them
 through the LM head with a bf16 MFMA GEMM whose epilogue streams the
 vocabulary (running max / argmax / sum of exponentials, so no L x V logits
-tensor exists), and commits the k most confident positions.  The work runs
+tensor exists), and commits the k best positions by confidence, top-2
+margin or negative entropy (top-k, or every position above a threshold).  The work runs
 in hand-written HIP kernels behind the C ABI in include/dllm_readout.h;
 this package is its thin Python binding.  PyTorch only provides device
 memory and streams.
@@ -17,6 +18,9 @@ from ._abi import (  # noqa: F401
     DLLM_ERR_WORKSPACE,
     DLLM_K_MAX_LIMIT,
     DLLM_OK,
+    DLLM_SCORE_CONF,
+    DLLM_SCORE_MARGIN,
+    DLLM_SCORE_NEG_ENTROPY,
     EXPORTED,
     LIB_PATH,
     DllmError,
@@ -25,9 +29,12 @@ from ._abi import (  # noqa: F401
     dllm_masked_readout_set_gemm_events,
     dllm_masked_readout_set_slices,
     dllm_masked_readout_step,
+    dllm_masked_readout_step_ex,
     dllm_masked_readout_workspace_bytes,
+    dllm_policy,
     dllm_status_string,
     load,
+    make_policy,
 )
 
 
@@ -60,27 +67,40 @@ class MaskedReadout:
         if st != DLLM_OK:
             raise DllmError(st, "dllm_masked_readout_set_slices")
 
-    def outputs(self):
-        """Freshly allocated output buffers for step()."""
+    def outputs(self, ext: bool = False):
+        """Freshly allocated output buffers for step(); ``ext`` adds the
+        per-row margin and entropy."""
         import torch
         dev = self.W_lm.device
         i32 = dict(dtype=torch.int32, device=dev)
         f32 = dict(dtype=torch.float32, device=dev)
         K, L = max(self.k_max, 1), self.L_max
-        return dict(n_out=torch.zeros(1, **i32), m_out=torch.zeros(1, **i32),
-                    sel_idx=torch.full((K,), -1, **i32), sel_tok=torch.full((K,), -1, **i32),
-                    sel_conf=torch.zeros(K, **f32), row_idx=torch.full((L,), -1, **i32),
-                    row_tok=torch.full((L,), -1, **i32), row_conf=torch.zeros(L, **f32),
-                    row_lse=torch.zeros(L, **f32))
+        o = dict(n_out=torch.zeros(1, **i32), m_out=torch.zeros(1, **i32),
+                 sel_idx=torch.full((K,), -1, **i32), sel_tok=torch.full((K,), -1, **i32),
+                 sel_conf=torch.zeros(K, **f32), row_idx=torch.full((L,), -1, **i32),
+                 row_tok=torch.full((L,), -1, **i32), row_conf=torch.zeros(L, **f32),
+                 row_lse=torch.zeros(L, **f32))
+        if ext:
+            o["row_margin"] = torch.zeros(L, **f32)
+            o["row_entropy"] = torch.zeros(L, **f32)
+        return o
 
     def step(self, hidden, mask, tokens, k: int, win_lo: int = 0, win_hi: int | None = None,
-             block: int = 0, out: dict | None = None) -> None:
-        """Queue one readout step on the handle's stream (asynchronous)."""
+             block: int = 0, out: dict | None = None, score="conf", tau: float | None = None) -> None:
+        """Queue one readout step on the handle's stream (asynchronous).
+
+        ``score`` ranks the candidates ("conf", "margin", "neg_entropy");
+        ``tau`` None commits the top k, otherwise every candidate whose score
+        is >= tau (at least one, at most k)."""
         L = int(hidden.shape[0])
         if win_hi is None:
             win_hi = L
-        st = dllm_masked_readout_step(self.handle, hidden, L, mask, tokens, int(k), int(win_lo), int(win_hi),
-                                      int(block), out)
+        if score == "conf" and tau is None:
+            st = dllm_masked_readout_step(self.handle, hidden, L, mask, tokens, int(k), int(win_lo),
+                                          int(win_hi), int(block), out)
+        else:
+            st = dllm_masked_readout_step_ex(self.handle, hidden, L, mask, tokens, int(k), int(win_lo),
+                                             int(win_hi), int(block), make_policy(score, tau), out)
         if st != DLLM_OK:
             raise DllmError(st, "dllm_masked_readout_step")
 

@@ -20,10 +20,16 @@ DLLM_ERR_WORKSPACE = 3
 DLLM_ERR_HIP = 4
 DLLM_K_MAX_LIMIT = 4096
 
+DLLM_SCORE_CONF = 0
+DLLM_SCORE_MARGIN = 1
+DLLM_SCORE_NEG_ENTROPY = 2
+SCORES = {"conf": DLLM_SCORE_CONF, "margin": DLLM_SCORE_MARGIN, "neg_entropy": DLLM_SCORE_NEG_ENTROPY}
+
 EXPORTED = (
     "dllm_masked_readout_workspace_bytes",
     "dllm_masked_readout_create",
     "dllm_masked_readout_step",
+    "dllm_masked_readout_step_ex",
     "dllm_masked_readout_destroy",
     "dllm_status_string",
     "dllm_masked_readout_set_slices",
@@ -42,6 +48,16 @@ class dllm_step_out(C.Structure):
         ("row_tok", C.c_void_p),
         ("row_conf", C.c_void_p),
         ("row_lse", C.c_void_p),
+        ("row_margin", C.c_void_p),
+        ("row_entropy", C.c_void_p),
+    ]
+
+
+class dllm_policy(C.Structure):
+    _fields_ = [
+        ("score", C.c_int32),
+        ("use_threshold", C.c_int32),
+        ("tau", C.c_float),
     ]
 
 
@@ -65,6 +81,10 @@ def load(path: str = LIB_PATH):
     lib.dllm_masked_readout_step.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p,
                                              C.c_int32, C.c_int64, C.c_int64, C.c_int64,
                                              C.POINTER(dllm_step_out)]
+    lib.dllm_masked_readout_step_ex.restype = C.c_int
+    lib.dllm_masked_readout_step_ex.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p,
+                                                C.c_int32, C.c_int64, C.c_int64, C.c_int64,
+                                                C.POINTER(dllm_policy), C.POINTER(dllm_step_out)]
     lib.dllm_masked_readout_destroy.restype = C.c_int
     lib.dllm_masked_readout_destroy.argtypes = [C.c_void_p]
     lib.dllm_status_string.restype = C.c_char_p
@@ -124,6 +144,26 @@ def dllm_masked_readout_step(handle, hidden, L: int, mask, tokens, k: int, win_l
         so = dllm_step_out(**{key: _ptr(v) for key, v in out.items()})
     return load().dllm_masked_readout_step(handle, _ptr(hidden), L, _ptr(mask), _ptr(tokens), k, win_lo, win_hi,
                                            block, C.byref(so) if so is not None else None)
+
+
+def make_policy(score="conf", tau: float | None = None) -> dllm_policy:
+    """dllm_policy for a score name ("conf", "margin", "neg_entropy") or
+    dllm_score value; ``tau`` None = top-k, otherwise the threshold rule."""
+    sc = SCORES[score] if isinstance(score, str) else int(score)
+    if tau is None:
+        return dllm_policy(sc, 0, 0.0)
+    return dllm_policy(sc, 1, float(tau))
+
+
+def dllm_masked_readout_step_ex(handle, hidden, L: int, mask, tokens, k: int, win_lo: int, win_hi: int,
+                                block: int = 0, policy: dllm_policy | None = None,
+                                out: dict | None = None) -> int:
+    so = None
+    if out:
+        so = dllm_step_out(**{key: _ptr(v) for key, v in out.items()})
+    return load().dllm_masked_readout_step_ex(handle, _ptr(hidden), L, _ptr(mask), _ptr(tokens), k, win_lo,
+                                              win_hi, block, C.byref(policy) if policy is not None else None,
+                                              C.byref(so) if so is not None else None)
 
 
 def dllm_masked_readout_destroy(handle) -> int:

@@ -8,8 +8,10 @@
 // the vocabulary, walks the slice tile by tile in increasing vocabulary
 // order and keeps, per row, the running maximum m, the lowest index a that
 // attains it and s = sum exp(z - m) (the streaming form of max and
-// log-sum-exp), rescaling s whenever m grows.  One partial (m, a, s) per
-// (row, slice) is written; the merge kernel combines the slices.
+// log-sum-exp), rescaling s whenever m grows; with the extended statistics
+// also the second-largest logit and sum exp(z - m) (z - m) for the margin
+// and entropy scores (online_state.h).  One partial per (row, slice) is
+// written; the merge kernel combines the slices.
 //
 // MI355X mapping
 //   * bf16 MFMA v_mfma_f32_32x32x16_bf16: A operand = 32 vocabulary rows of
@@ -31,30 +33,19 @@
 
 #include <math.h>
 
+#include "online_state.h"
+
 namespace dllm {
 namespace {
 
 typedef short bf16x8 __attribute__((__vector_size__(8 * sizeof(short))));
 typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
 
-constexpr float kLog2e = 1.4426950408889634f;
-
 __device__ __forceinline__ int xcd_remap(int bid, int grid) {
   constexpr int kXcd = 8;
   const int per = grid / kXcd, rem = grid % kXcd;
   const int x = bid % kXcd, loc = bid / kXcd;
   return (x < rem) ? x * (per + 1) + loc : rem * (per + 1) + (x - rem) * per + loc;
-}
-
-// Merge two streaming states (m, a, s).  Ties on m keep the lower index.
-__device__ __forceinline__ void merge_state(float& m, int& a, float& s, float m2, int a2, float s2) {
-  const bool take2 = (m2 > m) || (m2 == m && a2 < a);
-  const float mn = fmaxf(m, m2);
-  const float e1 = (m == -INFINITY) ? 0.f : s * __builtin_amdgcn_exp2f((m - mn) * kLog2e);
-  const float e2 = (m2 == -INFINITY) ? 0.f : s2 * __builtin_amdgcn_exp2f((m2 - mn) * kLog2e);
-  a = take2 ? a2 : a;
-  m = mn;
-  s = e1 + e2;
 }
 
 template <int BM_, int BN_, int WM_, int WN_, bool STREAM_W_ = false>
@@ -78,14 +69,12 @@ struct Tile {
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * kBK + ((chunk ^ (row & 7)) << 3); }
 
-template <class T>
+template <class T, bool EXT>
 __global__ __launch_bounds__(T::NT) void k_gemm_online(const uint16_t* __restrict__ W,
                                                        const uint16_t* __restrict__ H, int d, int V,
                                                        const int32_t* __restrict__ idx,
                                                        const int32_t* __restrict__ ctr, int slices,
-                                                       int n_vt, float* __restrict__ part_m,
-                                                       int32_t* __restrict__ part_a,
-                                                       float* __restrict__ part_s) {
+                                                       int n_vt, Partials part) {
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][T::BN * kBK];
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][T::BM * kBK];
 
@@ -159,14 +148,9 @@ __global__ __launch_bounds__(T::NT) void k_gemm_online(const uint16_t* __restric
   };
 
   f32x16 acc[T::FV][T::FR];
-  float run_m[T::FR], run_s[T::FR];
-  int run_a[T::FR];
+  RowState run[T::FR];
 #pragma unroll
-  for (int fr = 0; fr < T::FR; ++fr) {
-    run_m[fr] = -INFINITY;
-    run_s[fr] = 0.f;
-    run_a[fr] = 0;
-  }
+  for (int fr = 0; fr < T::FR; ++fr) run[fr] = row_state_empty();
 #pragma unroll
   for (int fv = 0; fv < T::FV; ++fv)
 #pragma unroll
@@ -222,39 +206,16 @@ __global__ __launch_bounds__(T::NT) void k_gemm_online(const uint16_t* __restric
       // with (fv, e), so a strict '>' scan keeps the lowest index.
       const int v0 = vt * T::BN + wv * T::WV + 4 * frag_half;
       const bool full = (vt + 1) * T::BN <= V;
+      auto off = [](int i) { return (i >> 4) * 32 + 8 * ((i & 15) >> 2) + (i & 3); };
 #pragma unroll
       for (int fr = 0; fr < T::FR; ++fr) {
-        float tm = -INFINITY;
-        int ta = 0;
+        float z[T::FV * 16];
 #pragma unroll
-        for (int fv = 0; fv < T::FV; ++fv)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int v = v0 + fv * 32 + 8 * (e >> 2) + (e & 3);
-            const float z = acc[fv][fr][e];
-            if ((full || v < V) && z > tm) {
-              tm = z;
-              ta = v;
-            }
-          }
-        if (tm != -INFINITY) {
-          const float mn = fmaxf(run_m[fr], tm);
-          const float sc = mn * kLog2e;
-          float sum = 0.f;
-#pragma unroll
-          for (int fv = 0; fv < T::FV; ++fv)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-              const int v = v0 + fv * 32 + 8 * (e >> 2) + (e & 3);
-              const float t = __builtin_amdgcn_exp2f(fmaf(acc[fv][fr][e], kLog2e, -sc));
-              sum += (full || v < V) ? t : 0.f;
-            }
-          const float old = (run_m[fr] == -INFINITY) ? 0.f
-                                                     : run_s[fr] * __builtin_amdgcn_exp2f(run_m[fr] * kLog2e - sc);
-          run_s[fr] = old + sum;
-          run_a[fr] = (tm > run_m[fr]) ? ta : run_a[fr];
-          run_m[fr] = mn;
+        for (int i = 0; i < T::FV * 16; ++i) {
+          z[i] = acc[i >> 4][fr][i & 15];
+          if (!full && v0 + off(i) >= V) z[i] = -INFINITY;
         }
+        row_fold<EXT, T::FV * 16>(run[fr], z, v0, off);
       }
 #pragma unroll
       for (int fv = 0; fv < T::FV; ++fv)
@@ -273,48 +234,75 @@ __global__ __launch_bounds__(T::NT) void k_gemm_online(const uint16_t* __restric
   // Combine the two half-waves (same rows, interleaved vocabulary entries).
 #pragma unroll
   for (int fr = 0; fr < T::FR; ++fr) {
-    const float m2 = __shfl_xor(run_m[fr], 32);
-    const int a2 = __shfl_xor(run_a[fr], 32);
-    const float s2 = __shfl_xor(run_s[fr], 32);
-    merge_state(run_m[fr], run_a[fr], run_s[fr], m2, a2, s2);
+    RowState y;
+    y.m = __shfl_xor(run[fr].m, 32);
+    y.s = __shfl_xor(run[fr].s, 32);
+    y.m2 = __shfl_xor(run[fr].m2, 32);
+    y.t = __shfl_xor(run[fr].t, 32);
+    y.a = __shfl_xor(run[fr].a, 32);
+    row_merge<EXT>(run[fr], y);
   }
 
   // Combine the WN waves that share rows, in wave order, through LDS.
   float* xm = reinterpret_cast<float*>(&sA[0][0]);
   int* xa = reinterpret_cast<int*>(xm + T::WN * T::BM);
   float* xs = reinterpret_cast<float*>(xa + T::WN * T::BM);
-  static_assert(3 * T::WN * T::BM * 4 <= (int)sizeof(sA), "LDS exchange area too small");
+  float* xm2 = xs + T::WN * T::BM;
+  float* xt = xm2 + T::WN * T::BM;
+  static_assert(5 * T::WN * T::BM * 4 <= (int)sizeof(sA), "LDS exchange area too small");
   if (frag_half == 0) {
 #pragma unroll
     for (int fr = 0; fr < T::FR; ++fr) {
       const int r = wr * T::WR + fr * 32 + frag_row;
-      xm[wv * T::BM + r] = run_m[fr];
-      xa[wv * T::BM + r] = run_a[fr];
-      xs[wv * T::BM + r] = run_s[fr];
+      xm[wv * T::BM + r] = run[fr].m;
+      xa[wv * T::BM + r] = run[fr].a;
+      xs[wv * T::BM + r] = run[fr].s;
+      if (EXT) {
+        xm2[wv * T::BM + r] = run[fr].m2;
+        xt[wv * T::BM + r] = run[fr].t;
+      }
     }
   }
   __syncthreads();
   for (int r = tid; r < T::BM; r += T::NT) {
-    float m = xm[r], s = xs[r];
-    int a = xa[r];
+    RowState x;
+    x.m = xm[r];
+    x.a = xa[r];
+    x.s = xs[r];
+    x.m2 = EXT ? xm2[r] : -INFINITY;
+    x.t = EXT ? xt[r] : 0.f;
 #pragma unroll
-    for (int w = 1; w < T::WN; ++w) merge_state(m, a, s, xm[w * T::BM + r], xa[w * T::BM + r], xs[w * T::BM + r]);
+    for (int w = 1; w < T::WN; ++w) {
+      RowState y;
+      y.m = xm[w * T::BM + r];
+      y.a = xa[w * T::BM + r];
+      y.s = xs[w * T::BM + r];
+      y.m2 = EXT ? xm2[w * T::BM + r] : -INFINITY;
+      y.t = EXT ? xt[w * T::BM + r] : 0.f;
+      row_merge<EXT>(x, y);
+    }
     const int row = row0 + r;
     if (row < M) {
       const size_t o = (size_t)row * (size_t)slices + (size_t)slice;
       if constexpr (T::STREAM_W) {
-        // few rows: one 16-byte record (m, a, s, 0) per partial in part_m,
-        // so the single-workgroup finish issues one load per partial
+        // few rows: one 16-byte record (m, a, s, 0) per partial in part.m
+        // (and (m2, t) in part.m2), so the single-workgroup finish issues
+        // one load per partial and array
         float4 rec;
-        rec.x = m;
-        rec.y = __int_as_float(a);
-        rec.z = s;
+        rec.x = x.m;
+        rec.y = __int_as_float(x.a);
+        rec.z = x.s;
         rec.w = 0.f;
-        reinterpret_cast<float4*>(part_m)[o] = rec;
+        reinterpret_cast<float4*>(part.m)[o] = rec;
+        if (EXT) reinterpret_cast<float2*>(part.m2)[o] = make_float2(x.m2, x.t);
       } else {
-        part_m[o] = m;
-        part_a[o] = a;
-        part_s[o] = s;
+        part.m[o] = x.m;
+        part.a[o] = x.a;
+        part.s[o] = x.s;
+        if (EXT) {
+          part.m2[o] = x.m2;
+          part.t[o] = x.t;
+        }
       }
     }
   }
@@ -329,21 +317,27 @@ using SmallTile = Tile<kSmallBM, kSmallBN, 1, 4, true>;
 }  // namespace
 
 hipError_t launch_gemm_large(const uint16_t* W, const uint16_t* H, int d, int V, const int32_t* idx,
-                             const int32_t* ctr, int n_row_tiles, int slices, float* pm, int32_t* pa,
-                             float* ps, hipStream_t stream) {
+                             const int32_t* ctr, int n_row_tiles, int slices, Partials p, hipStream_t stream) {
   const int n_vt = (V + LargeTile::BN - 1) / LargeTile::BN;
   const int grid = n_row_tiles * slices;
-  hipLaunchKernelGGL(k_gemm_online<LargeTile>, dim3(grid), dim3(LargeTile::NT), 0, stream, W, H, d, V,
-                     idx, ctr, slices, n_vt, pm, pa, ps);
+  if (p.ext)
+    hipLaunchKernelGGL((k_gemm_online<LargeTile, true>), dim3(grid), dim3(LargeTile::NT), 0, stream, W, H, d, V,
+                       idx, ctr, slices, n_vt, p);
+  else
+    hipLaunchKernelGGL((k_gemm_online<LargeTile, false>), dim3(grid), dim3(LargeTile::NT), 0, stream, W, H, d, V,
+                       idx, ctr, slices, n_vt, p);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_small(const uint16_t* W, const uint16_t* H, int d, int V, const int32_t* idx,
-                             const int32_t* ctr, int slices, float* pm, int32_t* pa, float* ps,
-                             hipStream_t stream) {
+                             const int32_t* ctr, int slices, Partials p, hipStream_t stream) {
   const int n_vt = (V + SmallTile::BN - 1) / SmallTile::BN;
-  hipLaunchKernelGGL(k_gemm_online<SmallTile>, dim3(slices), dim3(SmallTile::NT), 0, stream, W, H, d, V,
-                     idx, ctr, slices, n_vt, pm, pa, ps);
+  if (p.ext)
+    hipLaunchKernelGGL((k_gemm_online<SmallTile, true>), dim3(slices), dim3(SmallTile::NT), 0, stream, W, H, d, V,
+                       idx, ctr, slices, n_vt, p);
+  else
+    hipLaunchKernelGGL((k_gemm_online<SmallTile, false>), dim3(slices), dim3(SmallTile::NT), 0, stream, W, H, d, V,
+                       idx, ctr, slices, n_vt, p);
   return hipGetLastError();
 }
 

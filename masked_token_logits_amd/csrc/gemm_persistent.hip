@@ -1,7 +1,8 @@
 // Persistent, compute-bound masked LM-head GEMM with the fused online
 // vocabulary reduction (same arithmetic as the streaming GEMM in
 // gemm_online.hip: per row the running max m, the lowest index a attaining
-// it and s = sum exp(z - m) over the vocabulary in increasing order; Mosaic,
+// it and s = sum exp(z - m) over the vocabulary in increasing order, plus
+// the margin / entropy terms when asked for (online_state.h); Mosaic,
 // Abstract: logits only for masked positions, never materialised).
 //
 // MI355X mapping
@@ -37,6 +38,8 @@
 
 #include <type_traits>
 
+#include "online_state.h"
+
 namespace dllm {
 namespace {
 
@@ -50,7 +53,6 @@ constexpr int TILE = BM * BK;                 // elements of one operand tile pe
 constexpr int DMA_ROWS = 16;                  // rows written by one wave-wide DMA (64 x 16 B)
 constexpr int DMA_PER_OPERAND = BM / DMA_ROWS / 4;  // per wave per stage: 4
 constexpr int DMA_PER_STAGE = 2 * DMA_PER_OPERAND;  // per wave per stage: 8
-constexpr float kLog2e = 1.4426950408889634f;
 static_assert(BM == BN, "square tile assumed by the loader");
 static_assert(BK == 32, "swizzle and DMA layout assume 4 chunks of 16 B per row");
 
@@ -96,16 +98,6 @@ __device__ __forceinline__ void item_coords(int e, int n_rt, int S, int& rt, int
   slice = h * kGroupSlices + c;
 }
 
-__device__ __forceinline__ void merge_state(float& m, int& a, float& s, float m2, int a2, float s2) {
-  const bool take2 = (m2 > m) || (m2 == m && a2 < a);
-  const float mn = fmaxf(m, m2);
-  const float e1 = (m == -INFINITY) ? 0.f : s * __builtin_amdgcn_exp2f((m - mn) * kLog2e);
-  const float e2 = (m2 == -INFINITY) ? 0.f : s2 * __builtin_amdgcn_exp2f((m2 - mn) * kLog2e);
-  a = take2 ? a2 : a;
-  m = mn;
-  s = e1 + e2;
-}
-
 // Wait until at most N of this wave's vector-memory operations are
 // outstanding and all its LDS operations are done, then barrier the
 // workgroup.  The empty asm statements keep the compiler from moving memory
@@ -119,13 +111,11 @@ __device__ __forceinline__ void stage_sync() {
   asm volatile("" ::: "memory");
 }
 
+template <bool EXT>
 __global__ __launch_bounds__(NT, 1) void k_gemm_persistent(const uint16_t* __restrict__ W,
                                                           const uint16_t* __restrict__ H, int d, int V,
                                                           const int32_t* __restrict__ idx,
-                                                          const int32_t* __restrict__ ctr,
-                                                          float* __restrict__ part_m,
-                                                          int32_t* __restrict__ part_a,
-                                                          float* __restrict__ part_s) {
+                                                          const int32_t* __restrict__ ctr, Partials part) {
   __shared__ __attribute__((aligned(1024))) uint16_t lds[NST][2][TILE];
 
   const int M = ctr[0];
@@ -219,14 +209,35 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_persistent(const uint16_t* __res
       advance_issue();
     };
 
-    float run_m[4], run_s[4];
+    // Running state per row block, one array per field (an array of
+    // RowState structs is not split into registers and lands in scratch).
+    float run_m[4], run_s[4], run_m2[4], run_t[4];
     int run_a[4];
 #pragma unroll
     for (int fr = 0; fr < 4; ++fr) {
-      run_m[fr] = -INFINITY;
-      run_s[fr] = 0.f;
-      run_a[fr] = 0;
+      const RowState e0 = row_state_empty();
+      run_m[fr] = e0.m;
+      run_s[fr] = e0.s;
+      run_m2[fr] = e0.m2;
+      run_t[fr] = e0.t;
+      run_a[fr] = e0.a;
     }
+    auto get = [&](int fr) {
+      RowState r;
+      r.m = run_m[fr];
+      r.s = run_s[fr];
+      r.m2 = run_m2[fr];
+      r.t = run_t[fr];
+      r.a = run_a[fr];
+      return r;
+    };
+    auto put = [&](int fr, const RowState& r) {
+      run_m[fr] = r.m;
+      run_s[fr] = r.s;
+      run_m2[fr] = r.m2;
+      run_t[fr] = r.t;
+      run_a[fr] = r.a;
+    };
 
     // Fragment loads of K step kk (0/1) of ring slot `slot`: fragment i
     // (i = 0..7) is W_lm block i/2 when i is even, hidden block i/2 when odd,
@@ -320,6 +331,7 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_persistent(const uint16_t* __res
                    "a"(acc[3][3]));
       const int v0 = vt * BN + wv * 128 + 4 * frag_half;
       const bool full = (vt + 1) * BN <= V;
+      auto off = [](int x) { return 8 * (x >> 2) + (x & 3); };
 #pragma unroll
       for (int fr = 0; fr < 4; ++fr) {
 #pragma unroll
@@ -328,26 +340,11 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_persistent(const uint16_t* __res
 #pragma unroll
           for (int x = 0; x < 16; ++x) {
             asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(z[x]) : "a"(acc[fv][fr][x]));
-            if (!full && v0 + fv * 32 + 8 * (x >> 2) + (x & 3) >= V) z[x] = -INFINITY;
+            if (!full && v0 + fv * 32 + off(x) >= V) z[x] = -INFINITY;
           }
-          float bm = z[0];
-          int bi = 0;
-#pragma unroll
-          for (int x = 1; x < 16; ++x) {
-            bi = z[x] > bm ? (8 * (x >> 2) + (x & 3)) : bi;
-            bm = fmaxf(bm, z[x]);
-          }
-          const float mn = fmaxf(run_m[fr], bm);
-          if (mn != -INFINITY) {
-            const float sc = mn * kLog2e;
-            float sum = 0.f;
-#pragma unroll
-            for (int x = 0; x < 16; ++x) sum += __builtin_amdgcn_exp2f(fmaf(z[x], kLog2e, -sc));
-            const float old = (run_m[fr] == -INFINITY) ? 0.f : run_s[fr] * __builtin_amdgcn_exp2f(fmaf(run_m[fr], kLog2e, -sc));
-            run_s[fr] = old + sum;
-            run_a[fr] = (bm > run_m[fr]) ? v0 + fv * 32 + bi : run_a[fr];
-            run_m[fr] = mn;
-          }
+          RowState r = get(fr);
+          row_fold<EXT, 16>(r, z, v0 + fv * 32, off);
+          put(fr, r);
         }
       }
     }
@@ -355,10 +352,14 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_persistent(const uint16_t* __res
     // Half-waves hold the same rows with interleaved vocabulary entries.
 #pragma unroll
     for (int fr = 0; fr < 4; ++fr) {
-      const float m2 = __shfl_xor(run_m[fr], 32);
-      const int a2 = __shfl_xor(run_a[fr], 32);
-      const float s2 = __shfl_xor(run_s[fr], 32);
-      merge_state(run_m[fr], run_a[fr], run_s[fr], m2, a2, s2);
+      RowState x = get(fr), y;
+      y.m = __shfl_xor(x.m, 32);
+      y.s = __shfl_xor(x.s, 32);
+      y.m2 = __shfl_xor(x.m2, 32);
+      y.t = __shfl_xor(x.t, 32);
+      y.a = __shfl_xor(x.a, 32);
+      row_merge<EXT>(x, y);
+      put(fr, x);
     }
     // The two vocabulary halves (wv = 0, 1) of each row meet in LDS.  All DMAs
     // have landed (the last stage waited for vmcnt(0)); barrier before reuse.
@@ -366,6 +367,8 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_persistent(const uint16_t* __res
     float* xm = reinterpret_cast<float*>(&lds[0][0][0]);
     int* xa = reinterpret_cast<int*>(xm + 2 * BM);
     float* xs = reinterpret_cast<float*>(xa + 2 * BM);
+    float* xm2 = xs + 2 * BM;
+    float* xt = xm2 + 2 * BM;
     if (frag_half == 0) {
 #pragma unroll
       for (int fr = 0; fr < 4; ++fr) {
@@ -373,20 +376,37 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_persistent(const uint16_t* __res
         xm[wv * BM + r] = run_m[fr];
         xa[wv * BM + r] = run_a[fr];
         xs[wv * BM + r] = run_s[fr];
+        if (EXT) {
+          xm2[wv * BM + r] = run_m2[fr];
+          xt[wv * BM + r] = run_t[fr];
+        }
       }
     }
     stage_sync<0>();
     {
       const int r = tid;  // NT == BM: one row per thread
-      float m = xm[r], s = xs[r];
-      int a = xa[r];
-      merge_state(m, a, s, xm[BM + r], xa[BM + r], xs[BM + r]);
+      RowState x, y;
+      x.m = xm[r];
+      x.a = xa[r];
+      x.s = xs[r];
+      x.m2 = EXT ? xm2[r] : -INFINITY;
+      x.t = EXT ? xt[r] : 0.f;
+      y.m = xm[BM + r];
+      y.a = xa[BM + r];
+      y.s = xs[BM + r];
+      y.m2 = EXT ? xm2[BM + r] : -INFINITY;
+      y.t = EXT ? xt[BM + r] : 0.f;
+      row_merge<EXT>(x, y);
       const int row = row0 + r;
       if (row < M) {
         const size_t o = (size_t)row * (size_t)S + (size_t)slice;
-        part_m[o] = m;
-        part_a[o] = a;
-        part_s[o] = s;
+        part.m[o] = x.m;
+        part.a[o] = x.a;
+        part.s[o] = x.s;
+        if (EXT) {
+          part.m2[o] = x.m2;
+          part.t[o] = x.t;
+        }
       }
     }
     // The next item's prologue overwrites the exchange area and counts vmcnt
@@ -400,9 +420,11 @@ static_assert(NT == BM, "one thread per row in the final merge");
 }  // namespace
 
 hipError_t launch_gemm_persistent(const uint16_t* W, const uint16_t* H, int d, int V, const int32_t* idx,
-                                  const int32_t* ctr, int grid, float* pm, int32_t* pa, float* ps,
-                                  hipStream_t stream) {
-  hipLaunchKernelGGL(k_gemm_persistent, dim3(grid), dim3(NT), 0, stream, W, H, d, V, idx, ctr, pm, pa, ps);
+                                  const int32_t* ctr, int grid, Partials p, hipStream_t stream) {
+  if (p.ext)
+    hipLaunchKernelGGL(k_gemm_persistent<true>, dim3(grid), dim3(NT), 0, stream, W, H, d, V, idx, ctr, p);
+  else
+    hipLaunchKernelGGL(k_gemm_persistent<false>, dim3(grid), dim3(NT), 0, stream, W, H, d, V, idx, ctr, p);
   return hipGetLastError();
 }
 

@@ -1,92 +1,117 @@
-// Cross-slice merge and top-k commit.
+// Cross-slice merge and selection + commit.
 //
 // Merge: each row's per-slice partials (m_s, a_s, s_s) become
 //   m* = max_s m_s,  a* = lowest a_s among slices with m_s = m*,
 //   S  = sum_s s_s * exp(m_s - m*),  lse = m* + ln S,  conf = 1 / S,
-// i.e. the softmax probability of the argmax token, exp(m* - lse).  The row
-// also gets a 64-bit selection key: conf's float bits (positive floats order
-// like their bit patterns) above (0xFFFFFFFF - row), so larger keys mean
-// higher confidence and, on equal confidence, the lower row -- the lower
-// position, since rows are in position order.
+// i.e. the softmax probability of the argmax token, exp(m* - lse); with the
+// extended statistics also the second-largest logit and the entropy
+// (online_state.h).  The row gets a 64-bit selection key: its ranking score
+// mapped to an order-preserving 32-bit pattern, above (0xFFFFFFFF - row), so
+// larger keys mean a larger score and, on equal scores, the lower row --
+// the lower position, since rows are in position order.
 //
-// Select + commit: the n = min(k, M) largest keys (confidence-driven
-// unmasking: Accelerating Masked Diffusion Large Language Models: A Survey of
-// Efficient Inference Techniques, Main Findings) are found by an MSB-first
-// radix select with 8-bit digits in one workgroup, gathered, sorted
-// descending (bitonic, in LDS) and committed: tokens[pos] = argmax token,
-// mask[pos] = 0 -- the update set of the step, nothing else is written
-// (survey, Main Findings: Delta_t).
+// Select + commit: n rows are committed -- n = min(k, M) for top-k
+// (confidence-driven unmasking: Accelerating Masked Diffusion Large Language
+// Models: A Survey of Efficient Inference Techniques, Main Findings), or the
+// rows whose score clears tau, at least one and at most k (adaptive parallel
+// decoding: Dynamic-dLLM, abstract).  The n largest keys are found by an
+// MSB-first radix select with 8-bit digits in one workgroup, gathered,
+// sorted descending (bitonic, in LDS) and committed: tokens[pos] = argmax
+// token, mask[pos] = 0 -- the update set of the step, nothing else is
+// written (survey, Main Findings: Delta_t).
 #include "readout_internal.h"
 
 #include <math.h>
 
+#include "online_state.h"
+
 namespace dllm {
 namespace {
 
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
+__device__ __forceinline__ RowState shfl_xor_state(const RowState& r, int off) {
+  RowState y;
+  y.m = __shfl_xor(r.m, off);
+  y.s = __shfl_xor(r.s, off);
+  y.m2 = __shfl_xor(r.m2, off);
+  y.t = __shfl_xor(r.t, off);
+  y.a = __shfl_xor(r.a, off);
+  return y;
+}
 
-__device__ __forceinline__ void merge_state(float& m, int& a, float& s, float m2, int a2, float s2) {
-  const bool take2 = (m2 > m) || (m2 == m && a2 < a);
-  const float mn = fmaxf(m, m2);
-  const float e1 = (m == -INFINITY) ? 0.f : s * __builtin_amdgcn_exp2f((m - mn) * kLog2e);
-  const float e2 = (m2 == -INFINITY) ? 0.f : s2 * __builtin_amdgcn_exp2f((m2 - mn) * kLog2e);
-  a = take2 ? a2 : a;
-  m = mn;
-  s = e1 + e2;
+__device__ __forceinline__ uint64_t select_key(float score, int row) {
+  // + 0.f maps -0 to +0, so equal scores have equal keys
+  return ((uint64_t)float_order_key(score + 0.f) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)row);
 }
 
 constexpr int kMergeWaves = 4;
 
-__global__ __launch_bounds__(kMergeWaves * 64) void k_merge(
-    const int32_t* __restrict__ ctr, const int32_t* __restrict__ idx, const float* __restrict__ pm,
-    const int32_t* __restrict__ pa, const float* __restrict__ ps,
-    int32_t* __restrict__ row_tok, float* __restrict__ row_conf, float* __restrict__ row_lse,
-    uint64_t* __restrict__ keys, int32_t* o_row_idx, int32_t* o_row_tok, float* o_row_conf,
-    float* o_row_lse) {
+// One wave per row: lanes merge strided slices, then a butterfly.
+template <bool EXT>
+__global__ __launch_bounds__(kMergeWaves * 64) void k_merge(const int32_t* __restrict__ ctr,
+                                                          const int32_t* __restrict__ idx, Partials p, int score,
+                                                          int32_t* __restrict__ row_tok,
+                                                          float* __restrict__ row_conf,
+                                                          float* __restrict__ row_lse,
+                                                          uint64_t* __restrict__ keys, dllm_step_out o) {
   const int M = ctr[0];
   const int slices = ctr[3];
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * kMergeWaves + (threadIdx.x >> 6);
   if (row >= M) return;
   const size_t base = (size_t)row * (size_t)slices;
-  float m = -INFINITY, s = 0.f;
-  int a = 0x7FFFFFFF;
-  for (int j = lane; j < slices; j += 64) merge_state(m, a, s, pm[base + j], pa[base + j], ps[base + j]);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float m2 = __shfl_xor(m, off);
-    const int a2 = __shfl_xor(a, off);
-    const float s2 = __shfl_xor(s, off);
-    merge_state(m, a, s, m2, a2, s2);
+  RowState r = row_state_empty();
+  for (int j = lane; j < slices; j += 64) {
+    RowState y;
+    y.m = p.m[base + j];
+    y.a = p.a[base + j];
+    y.s = p.s[base + j];
+    y.m2 = EXT ? p.m2[base + j] : -INFINITY;
+    y.t = EXT ? p.t[base + j] : 0.f;
+    row_merge<EXT>(r, y);
   }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) row_merge<EXT>(r, shfl_xor_state(r, off));
   if (lane == 0) {
-    const float conf = 1.0f / s;
-    const float lse = m + __builtin_amdgcn_logf(s) * kLn2;
-    row_tok[row] = a;
-    row_conf[row] = conf;
-    row_lse[row] = lse;
-    keys[row] = ((uint64_t)__float_as_uint(conf) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)row);
-    if (o_row_idx) o_row_idx[row] = idx[row];
-    if (o_row_tok) o_row_tok[row] = a;
-    if (o_row_conf) o_row_conf[row] = conf;
-    if (o_row_lse) o_row_lse[row] = lse;
+    const RowStats st = row_finish<EXT>(r);
+    row_tok[row] = r.a;
+    row_conf[row] = st.conf;
+    row_lse[row] = st.lse;
+    keys[row] = select_key(policy_score(st, score), row);
+    if (o.row_idx) o.row_idx[row] = idx[row];
+    if (o.row_tok) o.row_tok[row] = r.a;
+    if (o.row_conf) o.row_conf[row] = st.conf;
+    if (o.row_lse) o.row_lse[row] = st.lse;
+    if (EXT && o.row_margin) o.row_margin[row] = st.margin;
+    if (EXT && o.row_entropy) o.row_entropy[row] = st.entropy;
   }
 }
 
 constexpr int kSelThreads = 1024;
 
 __global__ __launch_bounds__(kSelThreads) void k_topk_scatter(
-    const int32_t* __restrict__ ctr, int k, const uint64_t* __restrict__ keys,
-    const int32_t* __restrict__ idx, const int32_t* __restrict__ row_tok, uint8_t* __restrict__ mask,
-    int32_t* __restrict__ tokens, int32_t* n_out, int32_t* m_out, int32_t* sel_idx, int32_t* sel_tok,
-    float* sel_conf) {
+    const int32_t* __restrict__ ctr, int k, Policy pol, const uint64_t* __restrict__ keys,
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ row_tok, const float* __restrict__ row_conf,
+    uint8_t* __restrict__ mask, int32_t* __restrict__ tokens, int32_t* n_out, int32_t* m_out, int32_t* sel_idx,
+    int32_t* sel_tok, float* sel_conf) {
   __shared__ uint32_t hist[256];
   __shared__ uint64_t sel[kTopkCap];
   __shared__ int s_digit, s_remaining, s_done, s_count;
   const int tid = threadIdx.x;
   const int M = ctr[0];
-  const int n = k < M ? k : M;
+  int n = k < M ? k : M;
+  if (pol.use_threshold && n > 0) {
+    // rows whose score is >= tau: their key's high word is >= tau's pattern
+    const uint32_t tk = float_order_key(pol.tau + 0.f);
+    if (tid == 0) s_count = 0;
+    __syncthreads();
+    int c = 0;
+    for (int i = tid; i < M; i += kSelThreads) c += (uint32_t)(keys[i] >> 32) >= tk ? 1 : 0;
+    if (c) atomicAdd(&s_count, c);
+    __syncthreads();
+    const int cnt = s_count;
+    __syncthreads();
+    n = cnt < 1 ? 1 : (cnt < n ? cnt : n);
+  }
   if (tid == 0) {
     if (n_out) *n_out = n;
     if (m_out) *m_out = M;
@@ -171,85 +196,98 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_scatter(
     mask[pos] = 0;
     if (sel_idx) sel_idx[i] = pos;
     if (sel_tok) sel_tok[i] = tok;
-    if (sel_conf) sel_conf[i] = __uint_as_float((uint32_t)(key >> 32));
+    if (sel_conf) sel_conf[i] = row_conf[row];
   }
 }
 
 // Few rows (<= kSmallBM, the semi-autoregressive block): one workgroup
 // merges every row's slices (16-byte (m, a, s, 0) records written by the
-// streaming GEMM into pm; 32 lanes per row, loads issued 16 at a time
-// so their latencies overlap, then a butterfly), ranks the rows by counting
-// (row r precedes r' iff its confidence is larger, or equal with the lower
-// row = lower position) and commits the first n = min(k, M).
+// streaming GEMM into p.m, plus (m2, t) records in p.m2 for the extended
+// statistics; 32 lanes per row, loads issued U at a time so their
+// latencies overlap, then a butterfly), ranks the rows by counting (row r
+// precedes r' iff its score is larger, or equal with the lower row = lower
+// position) and commits the first n.
 constexpr int kFinishThreads = 1024;
 static_assert(kFinishThreads == 32 * kSmallBM, "32 lanes per row");
+template <bool EXT>
 __global__ __launch_bounds__(kFinishThreads) void k_finish_small(const int32_t* __restrict__ ctr,
-                                                                const int32_t* __restrict__ idx,
-                                                                const float* __restrict__ pm,
-                                                                const int32_t* __restrict__ pa,
-                                                                const float* __restrict__ ps, int k,
-                                                                uint8_t* __restrict__ mask,
+                                                                const int32_t* __restrict__ idx, Partials p,
+                                                                Policy pol, int k, uint8_t* __restrict__ mask,
                                                                 int32_t* __restrict__ tokens, dllm_step_out o) {
-  __shared__ float s_conf[kSmallBM], s_lse[kSmallBM];
+  __shared__ float s_conf[kSmallBM], s_lse[kSmallBM], s_score[kSmallBM], s_margin[kSmallBM], s_ent[kSmallBM];
   __shared__ int s_tok[kSmallBM];
   const int M = ctr[0];
   const int slices = ctr[3];
   const int r = threadIdx.x >> 5, sub = threadIdx.x & 31;
   if (r < M) {
     const size_t base = (size_t)r * (size_t)slices;
-    float m = -INFINITY, s = 0.f;
-    int a = 0x7FFFFFFF;
-    constexpr int U = 16;
+    RowState st = row_state_empty();
+    constexpr int U = EXT ? 8 : 16;
     for (int j0 = sub; j0 < slices; j0 += 32 * U) {
-      float mu[U], su[U];
-      int au[U];
+      float4 rec[U];
+      float2 rx[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int j = j0 + 32 * u;
-        float4 rec = make_float4(-INFINITY, __int_as_float(0x7FFFFFFF), 0.f, 0.f);
-        if (j < slices) rec = reinterpret_cast<const float4*>(pm)[base + j];
-        mu[u] = rec.x;
-        au[u] = __float_as_int(rec.y);
-        su[u] = rec.z;
+        rec[u] = make_float4(-INFINITY, __int_as_float(0x7FFFFFFF), 0.f, 0.f);
+        rx[u] = make_float2(-INFINITY, 0.f);
+        if (j < slices) {
+          rec[u] = reinterpret_cast<const float4*>(p.m)[base + j];
+          if (EXT) rx[u] = reinterpret_cast<const float2*>(p.m2)[base + j];
+        }
       }
 #pragma unroll
-      for (int u = 0; u < U; ++u) merge_state(m, a, s, mu[u], au[u], su[u]);
+      for (int u = 0; u < U; ++u) {
+        RowState y;
+        y.m = rec[u].x;
+        y.a = __float_as_int(rec[u].y);
+        y.s = rec[u].z;
+        y.m2 = rx[u].x;
+        y.t = rx[u].y;
+        row_merge<EXT>(st, y);
+      }
     }
 #pragma unroll
-    for (int off = 16; off >= 1; off >>= 1) {  // within the 32-lane half of the wave
-      const float m2 = __shfl_xor(m, off);
-      const int a2 = __shfl_xor(a, off);
-      const float s2 = __shfl_xor(s, off);
-      merge_state(m, a, s, m2, a2, s2);
-    }
+    for (int off = 16; off >= 1; off >>= 1) row_merge<EXT>(st, shfl_xor_state(st, off));  // 32-lane half
     if (sub == 0) {
-      s_conf[r] = 1.0f / s;
-      s_lse[r] = m + __builtin_amdgcn_logf(s) * kLn2;
-      s_tok[r] = a;
+      const RowStats f = row_finish<EXT>(st);
+      s_conf[r] = f.conf;
+      s_lse[r] = f.lse;
+      s_margin[r] = f.margin;
+      s_ent[r] = f.entropy;
+      s_score[r] = policy_score(f, pol.score) + 0.f;  // -0 -> +0
+      s_tok[r] = st.a;
     }
   }
   __syncthreads();
-  const int n = k < M ? k : M;
+  int n = k < M ? k : M;
   const int t = threadIdx.x;
+  if (pol.use_threshold && n > 0) {
+    int cnt = 0;
+    for (int r2 = 0; r2 < M; ++r2) cnt += s_score[r2] >= pol.tau ? 1 : 0;
+    n = cnt < 1 ? 1 : (cnt < n ? cnt : n);
+  }
   if (t < M) {
-    const float c = s_conf[t];
+    const float c = s_score[t];
     int rank = 0;
     for (int r2 = 0; r2 < M; ++r2) {
-      const float c2 = s_conf[r2];
+      const float c2 = s_score[r2];
       rank += (c2 > c || (c2 == c && r2 < t)) ? 1 : 0;
     }
     const int pos = idx[t];
     const int tok = s_tok[t];
     if (o.row_idx) o.row_idx[t] = pos;
     if (o.row_tok) o.row_tok[t] = tok;
-    if (o.row_conf) o.row_conf[t] = c;
+    if (o.row_conf) o.row_conf[t] = s_conf[t];
     if (o.row_lse) o.row_lse[t] = s_lse[t];
+    if (EXT && o.row_margin) o.row_margin[t] = s_margin[t];
+    if (EXT && o.row_entropy) o.row_entropy[t] = s_ent[t];
     if (rank < n) {
       tokens[pos] = tok;
       mask[pos] = 0;
       if (o.sel_idx) o.sel_idx[rank] = pos;
       if (o.sel_tok) o.sel_tok[rank] = tok;
-      if (o.sel_conf) o.sel_conf[rank] = c;
+      if (o.sel_conf) o.sel_conf[rank] = s_conf[t];
     }
   }
   if (t == 0) {
@@ -260,31 +298,37 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish_small(const int32_t* 
 
 }  // namespace
 
-hipError_t launch_finish_small(const int32_t* ctr, const int32_t* idx, const float* pm, const int32_t* pa,
-                               const float* ps, int k, uint8_t* mask, int32_t* tokens, dllm_step_out out,
-                               hipStream_t stream) {
-  hipLaunchKernelGGL(k_finish_small, dim3(1), dim3(kFinishThreads), 0, stream, ctr, idx, pm, pa, ps, k, mask, tokens,
-                     out);
+hipError_t launch_finish_small(const int32_t* ctr, const int32_t* idx, Partials p, Policy pol, int k,
+                               uint8_t* mask, int32_t* tokens, dllm_step_out out, hipStream_t stream) {
+  if (p.ext)
+    hipLaunchKernelGGL(k_finish_small<true>, dim3(1), dim3(kFinishThreads), 0, stream, ctr, idx, p, pol, k, mask,
+                       tokens, out);
+  else
+    hipLaunchKernelGGL(k_finish_small<false>, dim3(1), dim3(kFinishThreads), 0, stream, ctr, idx, p, pol, k, mask,
+                       tokens, out);
   return hipGetLastError();
 }
 
-hipError_t launch_merge(const int32_t* ctr, const int32_t* idx, const float* pm, const int32_t* pa,
-                        const float* ps, int max_rows, int32_t* row_tok, float* row_conf,
-                        float* row_lse, uint64_t* keys, int32_t* o_row_idx, int32_t* o_row_tok,
-                        float* o_row_conf, float* o_row_lse, hipStream_t stream) {
+hipError_t launch_merge(const int32_t* ctr, const int32_t* idx, Partials p, int score, int max_rows,
+                        int32_t* row_tok, float* row_conf, float* row_lse, uint64_t* keys,
+                        const dllm_step_out& out, hipStream_t stream) {
   const int grid = (max_rows + kMergeWaves - 1) / kMergeWaves;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_merge, dim3(grid), dim3(kMergeWaves * 64), 0, stream, ctr, idx, pm, pa, ps,
-                     row_tok, row_conf, row_lse, keys, o_row_idx, o_row_tok, o_row_conf, o_row_lse);
+  if (p.ext)
+    hipLaunchKernelGGL(k_merge<true>, dim3(grid), dim3(kMergeWaves * 64), 0, stream, ctr, idx, p, score, row_tok,
+                       row_conf, row_lse, keys, out);
+  else
+    hipLaunchKernelGGL(k_merge<false>, dim3(grid), dim3(kMergeWaves * 64), 0, stream, ctr, idx, p, score, row_tok,
+                       row_conf, row_lse, keys, out);
   return hipGetLastError();
 }
 
-hipError_t launch_topk_scatter(const int32_t* ctr, int k, const uint64_t* keys, const int32_t* idx,
-                               const int32_t* row_tok, uint8_t* mask, int32_t* tokens,
+hipError_t launch_topk_scatter(const int32_t* ctr, int k, Policy pol, const uint64_t* keys, const int32_t* idx,
+                               const int32_t* row_tok, const float* row_conf, uint8_t* mask, int32_t* tokens,
                                int32_t* n_out, int32_t* m_out, int32_t* sel_idx, int32_t* sel_tok,
                                float* sel_conf, hipStream_t stream) {
-  hipLaunchKernelGGL(k_topk_scatter, dim3(1), dim3(kSelThreads), 0, stream, ctr, k, keys, idx, row_tok,
-                     mask, tokens, n_out, m_out, sel_idx, sel_tok, sel_conf);
+  hipLaunchKernelGGL(k_topk_scatter, dim3(1), dim3(kSelThreads), 0, stream, ctr, k, pol, keys, idx, row_tok,
+                     row_conf, mask, tokens, n_out, m_out, sel_idx, sel_tok, sel_conf);
   return hipGetLastError();
 }
 

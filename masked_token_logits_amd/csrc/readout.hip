@@ -42,6 +42,7 @@ size_t carve(int64_t L_max, int64_t V, uint8_t* base, dllm::Workspace* ws) {
   const int64_t part_cap_large = (L_max + dllm::kLargeBM - 1) / dllm::kLargeBM * dllm::kLargeBM *
                                  dllm::kMaxLargeSlices;
   // the few-row path stores 16-byte (m, a, s, 0) records in part_m: 4 floats per partial
+  // (and 8-byte (m2, t) records in part_m2)
   const int64_t part_cap_small = 4 * (int64_t)dllm::kSmallBM * small_slice_count(V);
   const int64_t part_cap = part_cap_large > part_cap_small ? part_cap_large : part_cap_small;
   size_t off = 0;
@@ -56,6 +57,8 @@ size_t carve(int64_t L_max, int64_t V, uint8_t* base, dllm::Workspace* ws) {
   w.part_m = reinterpret_cast<float*>(take(sizeof(float) * (size_t)part_cap));
   w.part_a = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)part_cap));
   w.part_s = reinterpret_cast<float*>(take(sizeof(float) * (size_t)part_cap));
+  w.part_m2 = reinterpret_cast<float*>(take(sizeof(float) * (size_t)part_cap));
+  w.part_t = reinterpret_cast<float*>(take(sizeof(float) * (size_t)part_cap));
   w.row_tok = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)L_max));
   w.row_conf = reinterpret_cast<float*>(take(sizeof(float) * (size_t)L_max));
   w.row_lse = reinterpret_cast<float*>(take(sizeof(float) * (size_t)L_max));
@@ -150,7 +153,22 @@ dllm_status dllm_masked_readout_set_gemm_events(dllm_readout* h, void* ev_before
 dllm_status dllm_masked_readout_step(dllm_readout* h, const uint16_t* hidden, int64_t L, uint8_t* mask,
                                      int32_t* tokens, int32_t k, int64_t win_lo, int64_t win_hi,
                                      int64_t block, const dllm_step_out* out) {
+  return dllm_masked_readout_step_ex(h, hidden, L, mask, tokens, k, win_lo, win_hi, block, nullptr, out);
+}
+
+dllm_status dllm_masked_readout_step_ex(dllm_readout* h, const uint16_t* hidden, int64_t L, uint8_t* mask,
+                                        int32_t* tokens, int32_t k, int64_t win_lo, int64_t win_hi,
+                                        int64_t block, const dllm_policy* policy, const dllm_step_out* out) {
   if (!h || !hidden || !mask || !tokens) return DLLM_ERR_INVALID_ARG;
+  dllm::Policy pol = {DLLM_SCORE_CONF, 0, 0.f};
+  if (policy) {
+    if (policy->score < DLLM_SCORE_CONF || policy->score > DLLM_SCORE_NEG_ENTROPY) return DLLM_ERR_INVALID_ARG;
+    if (policy->use_threshold != 0 && policy->use_threshold != 1) return DLLM_ERR_INVALID_ARG;
+    if (policy->tau != policy->tau) return DLLM_ERR_INVALID_ARG;  // NaN
+    pol.score = policy->score;
+    pol.use_threshold = policy->use_threshold;
+    pol.tau = policy->tau + 0.f;  // -0 -> +0: the kernels compare order-preserving bit patterns
+  }
   if (L <= 0 || L > h->L_max) return DLLM_ERR_INVALID_ARG;
   if (k < 0 || k > h->k_max) return DLLM_ERR_INVALID_ARG;
   if (win_lo < 0 || win_lo > win_hi || win_hi > L) return DLLM_ERR_INVALID_ARG;
@@ -167,6 +185,9 @@ dllm_status dllm_masked_readout_step(dllm_readout* h, const uint16_t* hidden, in
   }
 
   const dllm::Workspace& w = h->ws;
+  // margin / entropy are needed for ranking or output: keep (m2, t) too
+  const bool ext = pol.score != DLLM_SCORE_CONF || o.row_margin != nullptr || o.row_entropy != nullptr;
+  const dllm::Partials parts = {w.part_m, w.part_a, w.part_s, w.part_m2, w.part_t, ext};
   const int64_t span = win_hi - win_lo;
   const int64_t rows_max = (block > 0 && block < span) ? block : span;  // upper bound on M
   const int V = (int)h->V, d = (int)h->d;
@@ -210,34 +231,30 @@ dllm_status dllm_masked_readout_step(dllm_readout* h, const uint16_t* hidden, in
     hipError_t e;
     if (h->ev_before && hipEventRecord(h->ev_before, st) != hipSuccess) return DLLM_ERR_HIP;
     if (path == kSmall) {
-      e = dllm::launch_gemm_small(h->W, hidden, d, V, w.idx, w.ctr, plan.fixed_slices, w.part_m, w.part_a,
-                                  w.part_s, st);
+      e = dllm::launch_gemm_small(h->W, hidden, d, V, w.idx, w.ctr, plan.fixed_slices, parts, st);
     } else if (path == kPersistent) {
-      e = dllm::launch_gemm_persistent(h->W, hidden, d, V, w.idx, w.ctr, h->cus, w.part_m, w.part_a, w.part_s,
-                                       st);
+      e = dllm::launch_gemm_persistent(h->W, hidden, d, V, w.idx, w.ctr, h->cus, parts, st);
     } else {
-      e = dllm::launch_gemm_large(h->W, hidden, d, V, w.idx, w.ctr, n_rt, plan.fixed_slices, w.part_m,
-                                  w.part_a, w.part_s, st);
+      e = dllm::launch_gemm_large(h->W, hidden, d, V, w.idx, w.ctr, n_rt, plan.fixed_slices, parts, st);
     }
     if (h->log)
-      fprintf(stderr, "[dllm] step rows<=%lld path=%s slices=%d cus=%d\n", (long long)rows_max,
-              path == kSmall ? "small" : path == kPersistent ? "persistent" : "streaming", plan.fixed_slices,
-              h->cus);
+      fprintf(stderr, "[dllm] step rows<=%lld path=%s slices=%d cus=%d ext=%d score=%d threshold=%d\n",
+              (long long)rows_max, path == kSmall ? "small" : path == kPersistent ? "persistent" : "streaming",
+              plan.fixed_slices, h->cus, (int)ext, pol.score, pol.use_threshold);
     if (e != hipSuccess) return DLLM_ERR_HIP;
     if (h->ev_after && hipEventRecord(h->ev_after, st) != hipSuccess) return DLLM_ERR_HIP;
     if (path == kSmall) {
       // merge, selection and commit of <= 32 rows in one workgroup
-      if (dllm::launch_finish_small(w.ctr, w.idx, w.part_m, w.part_a, w.part_s, k, mask, tokens, o, st) != hipSuccess)
+      if (dllm::launch_finish_small(w.ctr, w.idx, parts, pol, k, mask, tokens, o, st) != hipSuccess)
         return DLLM_ERR_HIP;
       return DLLM_OK;
     }
-    if (dllm::launch_merge(w.ctr, w.idx, w.part_m, w.part_a, w.part_s, (int)rows_max, w.row_tok,
-                           w.row_conf, w.row_lse, w.keys, o.row_idx, o.row_tok, o.row_conf, o.row_lse,
-                           st) != hipSuccess)
+    if (dllm::launch_merge(w.ctr, w.idx, parts, pol.score, (int)rows_max, w.row_tok, w.row_conf, w.row_lse,
+                           w.keys, o, st) != hipSuccess)
       return DLLM_ERR_HIP;
   }
-  if (dllm::launch_topk_scatter(w.ctr, k, w.keys, w.idx, w.row_tok, mask, tokens, o.n_out, o.m_out,
-                                o.sel_idx, o.sel_tok, o.sel_conf, st) != hipSuccess)
+  if (dllm::launch_topk_scatter(w.ctr, k, pol, w.keys, w.idx, w.row_tok, w.row_conf, mask, tokens, o.n_out,
+                                o.m_out, o.sel_idx, o.sel_tok, o.sel_conf, st) != hipSuccess)
     return DLLM_ERR_HIP;
   return DLLM_OK;
 }

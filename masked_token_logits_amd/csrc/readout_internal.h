@@ -17,11 +17,32 @@ struct Workspace {
   float* part_m;       // [part_cap] per (row, slice) running max logit
   int32_t* part_a;     // [part_cap] per (row, slice) argmax vocabulary index
   float* part_s;       // [part_cap] per (row, slice) sum of exp(z - part_m)
+  float* part_m2;      // [part_cap] extended statistics: second-largest logit
+  float* part_t;       // [part_cap] extended statistics: sum exp(z - part_m) * (z - part_m)
   int32_t* row_tok;    // [L_max]   merged argmax per candidate row
   float* row_conf;     // [L_max]   merged confidence
   float* row_lse;      // [L_max]   merged log-sum-exp
-  uint64_t* keys;      // [L_max]   selection key: conf bits << 32 | (0xFFFFFFFF - row)
+  uint64_t* keys;      // [L_max]   selection key: ordered score bits << 32 | (0xFFFFFFFF - row)
   int64_t part_cap;
+};
+
+// Partials of one step: (m, a, s) always, (m2, t) when `ext` (margin or
+// entropy requested).  The few-row path stores (m, a, s, 0) float4 records
+// in m and (m2, t) float2 records in m2.
+struct Partials {
+  float* m;
+  int32_t* a;
+  float* s;
+  float* m2;
+  float* t;
+  bool ext;
+};
+
+// Selection policy as the kernels see it (validated dllm_policy).
+struct Policy {
+  int score;          // 0 conf, 1 margin, 2 negative entropy
+  int use_threshold;  // 0 top-k, 1 threshold with cap k
+  float tau;
 };
 
 // Tile shapes of the two GEMM variants (rows = candidate rows, vocab = W_lm rows).
@@ -55,33 +76,28 @@ hipError_t launch_mask_compact_small(const uint8_t* mask, int64_t win_lo, int64_
                                      int fixed_slices, int32_t* idx, int32_t* ctr, hipStream_t stream);
 
 hipError_t launch_gemm_large(const uint16_t* W, const uint16_t* H, int d, int V, const int32_t* idx,
-                             const int32_t* ctr, int n_row_tiles, int slices, float* pm, int32_t* pa,
-                             float* ps, hipStream_t stream);
+                             const int32_t* ctr, int n_row_tiles, int slices, Partials p, hipStream_t stream);
 
 // Persistent compute-bound variant (d % 32 == 0): `grid` workgroups walk the
 // (row tile, slice) items of the device-side plan in ctr[3], ctr[4].
 constexpr int kPersistBM = 256, kPersistBN = 256, kPersistBK = 32, kPersistStages = 4;
 hipError_t launch_gemm_persistent(const uint16_t* W, const uint16_t* H, int d, int V, const int32_t* idx,
-                                  const int32_t* ctr, int grid, float* pm, int32_t* pa, float* ps,
-                                  hipStream_t stream);
+                                  const int32_t* ctr, int grid, Partials p, hipStream_t stream);
 
 hipError_t launch_gemm_small(const uint16_t* W, const uint16_t* H, int d, int V, const int32_t* idx,
-                             const int32_t* ctr, int slices, float* pm, int32_t* pa, float* ps,
-                             hipStream_t stream);
+                             const int32_t* ctr, int slices, Partials p, hipStream_t stream);
 
 // Merge + selection + commit for at most kSmallBM candidate rows, in one
 // workgroup (replaces launch_merge + launch_topk_scatter on the small path).
-hipError_t launch_finish_small(const int32_t* ctr, const int32_t* idx, const float* pm, const int32_t* pa,
-                               const float* ps, int k, uint8_t* mask, int32_t* tokens, dllm_step_out out,
-                               hipStream_t stream);
+hipError_t launch_finish_small(const int32_t* ctr, const int32_t* idx, Partials p, Policy pol, int k,
+                               uint8_t* mask, int32_t* tokens, dllm_step_out out, hipStream_t stream);
 
-hipError_t launch_merge(const int32_t* ctr, const int32_t* idx, const float* pm, const int32_t* pa,
-                        const float* ps, int max_rows, int32_t* row_tok, float* row_conf,
-                        float* row_lse, uint64_t* keys, int32_t* o_row_idx, int32_t* o_row_tok,
-                        float* o_row_conf, float* o_row_lse, hipStream_t stream);
+hipError_t launch_merge(const int32_t* ctr, const int32_t* idx, Partials p, int score, int max_rows,
+                        int32_t* row_tok, float* row_conf, float* row_lse, uint64_t* keys,
+                        const dllm_step_out& out, hipStream_t stream);
 
-hipError_t launch_topk_scatter(const int32_t* ctr, int k, const uint64_t* keys, const int32_t* idx,
-                               const int32_t* row_tok, uint8_t* mask, int32_t* tokens,
+hipError_t launch_topk_scatter(const int32_t* ctr, int k, Policy pol, const uint64_t* keys, const int32_t* idx,
+                               const int32_t* row_tok, const float* row_conf, uint8_t* mask, int32_t* tokens,
                                int32_t* n_out, int32_t* m_out, int32_t* sel_idx, int32_t* sel_tok,
                                float* sel_conf, hipStream_t stream);
 

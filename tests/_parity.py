@@ -11,6 +11,15 @@ excluded and counted rather than compared):
     agree outside the band of rows whose oracle log-confidence lies within
     GAP of that boundary, and hold exactly n positions.  Sets are compared,
     rank order only where the oracle's neighbouring scores differ by > GAP.
+  * margin and entropy (the other ranking scores): a relative error of REL
+    on a probability is an absolute error of REL on its logarithm, so the
+    entropy (an expectation of -log p) is held to REL nats absolute, and the
+    margin p1 - p2 to REL * (p1 + p2).  Selections ranked by them use the
+    same band rule with band widths MARGIN_GAP (probability) and
+    ENTROPY_GAP (nats).
+  * threshold selection: the library's n must equal the clamped count of its
+    own float32 scores >= tau (the same precision decides on both sides),
+    and lie between the oracle's counts at tau + gap and tau - gap.
 """
 from __future__ import annotations
 
@@ -18,6 +27,8 @@ import numpy as np
 
 GAP = 1e-3
 REL = 2e-3
+MARGIN_GAP = 2e-3
+ENTROPY_GAP = 2e-3
 
 
 def to_dev(W, H, mask, tokens):
@@ -30,20 +41,80 @@ def to_dev(W, H, mask, tokens):
     return Wt, Ht, mt, tt
 
 
-def run_step(rd, Ht, mt, tt, k, lo, hi, block=0):
-    """One step through the C ABI; returns host copies of every output."""
+def run_step(rd, Ht, mt, tt, k, lo, hi, block=0, score="conf", tau=None, ext=False):
+    """One step through the C ABI; returns host copies of every output
+    (``ext``: also the per-row margin and entropy)."""
     import torch
-    out = rd.outputs()
-    rd.step(Ht, mt, tt, k, lo, hi, block, out=out)
+    out = rd.outputs(ext=ext)
+    rd.step(Ht, mt, tt, k, lo, hi, block, out=out, score=score, tau=tau)
     torch.cuda.synchronize()
     n = int(out["n_out"].item())
     M = int(out["m_out"].item())
     res = dict(n=n, M=M, mask=mt.cpu().numpy(), tokens=tt.cpu().numpy())
     for key in ("sel_idx", "sel_tok", "sel_conf"):
         res[key] = out[key][:n].cpu().numpy()
-    for key in ("row_idx", "row_tok", "row_conf", "row_lse"):
-        res[key] = out[key][:M].cpu().numpy()
+    for key in ("row_idx", "row_tok", "row_conf", "row_lse", "row_margin", "row_entropy"):
+        if key in out:
+            res[key] = out[key][:M].cpu().numpy()
     return res
+
+
+def oracle_score(st, score):
+    """The oracle's ranking score per row (fp64)."""
+    return {"conf": st["logconf"], "margin": st["margin"], "neg_entropy": -st["entropy"]}[score]
+
+
+def score_gap(score):
+    """Band width of the selection rule for a score (in its own units)."""
+    return {"conf": GAP, "margin": MARGIN_GAP, "neg_entropy": ENTROPY_GAP}[score]
+
+
+def library_score(g, score):
+    """The library's float32 ranking score per row, as its kernels rank by."""
+    if score == "conf":
+        return g["row_conf"].astype(np.float32)
+    if score == "margin":
+        return g["row_margin"].astype(np.float32)
+    return -g["row_entropy"].astype(np.float32)
+
+
+def check_ext_rows(g_margin, g_entropy, st, where=""):
+    """Margin and entropy parity (tolerances in the module docstring)."""
+    p2 = st["conf"] - st["margin"]
+    for name, g, lim in (("margin", g_margin, REL * (st["conf"] + p2)),
+                         ("entropy", g_entropy, np.full(len(p2), REL))):
+        err = np.abs(np.asarray(g, np.float64) - st[name])
+        bad = np.flatnonzero(err > lim)
+        assert len(bad) == 0, f"{where}: {name} off at rows {bad[:10]}: gpu {np.asarray(g)[bad[:10]]} oracle {st[name][bad[:10]]}"
+
+
+def check_self_selection(g, score, k, tau=None, where=""):
+    """The commit is exactly the library's own top n by its float32 scores
+    (position ascending on ties), n = min(k, M) or the threshold rule."""
+    M = g["M"]
+    sc = library_score(g, score)
+    n = min(k, M)
+    if tau is not None and n > 0:
+        cnt = int(np.count_nonzero(sc >= np.float32(tau)))
+        n = min(max(cnt, 1), n)
+    assert g["n"] == n, f"{where}: n {g['n']} vs {n} from the library's own scores"
+    order = np.lexsort((g["row_idx"], -sc.astype(np.float64)))
+    np.testing.assert_array_equal(g["sel_idx"], g["row_idx"][order[:n]])
+    np.testing.assert_array_equal(g["sel_tok"], g["row_tok"][order[:n]])
+    np.testing.assert_array_equal(g["sel_conf"], g["row_conf"][order[:n]])
+    return n
+
+
+def threshold_n_bounds(score_o, tau, k, gap):
+    """Range of n that the threshold rule can give when scores carry an
+    error of up to ``gap``."""
+    M = len(score_o)
+    if M == 0 or k <= 0:
+        return 0, 0
+    cap = min(k, M)
+    lo = min(max(int(np.count_nonzero(score_o >= tau + gap)), 1), cap)
+    hi = min(max(int(np.count_nonzero(score_o >= tau - gap)), 1), cap)
+    return lo, hi
 
 
 def check_rows(g_tok, g_conf, g_lse, st, where=""):
@@ -62,13 +133,13 @@ def check_rows(g_tok, g_conf, g_lse, st, where=""):
 
 
 def oracle_rank(positions, logconf):
-    """Positions sorted by log-confidence descending, position ascending."""
+    """Positions sorted by score (log-confidence) descending, position ascending."""
     positions = np.asarray(positions, np.int64)
     order = np.lexsort((positions, -np.asarray(logconf, np.float64)))
     return positions[order], np.asarray(logconf, np.float64)[order]
 
 
-def check_selection(sel_g, positions, logconf, n, where=""):
+def check_selection(sel_g, positions, logconf, n, where="", gap=GAP):
     """Committed-set parity (see module docstring); returns the band size."""
     sel_g = [int(x) for x in sel_g]
     assert len(sel_g) == n == len(set(sel_g)), f"{where}: expected {n} distinct positions, got {len(sel_g)}"
@@ -80,20 +151,20 @@ def check_selection(sel_g, positions, logconf, n, where=""):
         assert set(sel_g) == sel_o, f"{where}: all candidates should commit"
         return 0
     c_n, c_n1 = lc[n - 1], lc[n]
-    if c_n - c_n1 > GAP:
+    if c_n - c_n1 > gap:
         assert set(sel_g) == sel_o, f"{where}: committed sets differ: {sorted(set(sel_g) ^ sel_o)[:10]}"
         return 0
-    band = set(int(p) for p, c in zip(ranked, lc) if c_n1 - GAP <= c <= c_n + GAP)
+    band = set(int(p) for p, c in zip(ranked, lc) if c_n1 - gap <= c <= c_n + gap)
     assert set(sel_g) - band == sel_o - band, f"{where}: committed sets differ outside the near-tie band"
     return len(band)
 
 
-def check_rank_order(sel_g, positions, logconf, where=""):
+def check_rank_order(sel_g, positions, logconf, where="", gap=GAP):
     """Rank order of the committed positions where the oracle separates them."""
     pos_to_lc = {int(p): float(c) for p, c in zip(positions, logconf)}
     lcs = [pos_to_lc[int(p)] for p in sel_g]
     for i in range(len(lcs) - 1):
-        if lcs[i + 1] - lcs[i] > GAP:
+        if lcs[i + 1] - lcs[i] > gap:
             raise AssertionError(f"{where}: rank {i} and {i + 1} out of order ({lcs[i]} < {lcs[i + 1]})")
 
 

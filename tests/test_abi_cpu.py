@@ -46,8 +46,9 @@ def test_status_strings(lib):
 
 def test_workspace_bytes():
     b = mtl.dllm_masked_readout_workspace_bytes(131072, 4096, 126464, 1024)
-    # O(L_max * slices) partials + O(L_max) row arrays; never O(L * V)
-    assert 0 < b < 131072 * 64 * 12 + 131072 * 40 + (1 << 20)
+    # O(L_max * slices) partials of 5 fields (m, a, s, m2, t) + O(L_max) row
+    # arrays; never O(L * V)
+    assert 0 < b < 131072 * 64 * 20 + 131072 * 40 + (1 << 20)
     assert mtl.dllm_masked_readout_workspace_bytes(0, 4096, 126464, 8) == 0
     assert mtl.dllm_masked_readout_workspace_bytes(10, 4096, 126464, -1) == 0
     assert mtl.dllm_masked_readout_workspace_bytes(10, 4096, 0, 8) == 0
@@ -114,6 +115,39 @@ def test_step_validation_before_any_hip_call():
     assert mtl.dllm_masked_readout_set_slices(h, 7) == E.DLLM_OK
     assert mtl.dllm_masked_readout_set_slices(None, 1) == E.DLLM_ERR_INVALID_ARG
     mtl.dllm_masked_readout_destroy(h)
+
+
+def test_step_ex_policy_validation_before_any_hip_call():
+    st, h = _create()
+    assert st == mtl.DLLM_OK
+    E = mtl
+    H, Mk, T = FAKE + 0x200000, FAKE + 0x300000, FAKE + 0x400000
+
+    def step(policy):
+        return mtl.dllm_masked_readout_step_ex(h, H, 256, Mk, T, 4, 0, 256, 0, policy)
+
+    assert step(_abi.dllm_policy(3, 0, 0.0)) == E.DLLM_ERR_INVALID_ARG       # unknown score
+    assert step(_abi.dllm_policy(-1, 0, 0.0)) == E.DLLM_ERR_INVALID_ARG
+    assert step(_abi.dllm_policy(0, 2, 0.0)) == E.DLLM_ERR_INVALID_ARG       # use_threshold not 0/1
+    assert step(_abi.dllm_policy(1, 1, float("nan"))) == E.DLLM_ERR_INVALID_ARG
+    # argument checks come first, also for step_ex
+    assert mtl.dllm_masked_readout_step_ex(h, H, 0, Mk, T, 4, 0, 256, 0, None) == E.DLLM_ERR_INVALID_ARG
+    assert mtl.dllm_masked_readout_step_ex(None, H, 256, Mk, T, 4, 0, 256, 0,
+                                           mtl.make_policy("margin", 0.5)) == E.DLLM_ERR_INVALID_ARG
+    p = mtl.make_policy("neg_entropy", -1.5)
+    assert (p.score, p.use_threshold) == (mtl.DLLM_SCORE_NEG_ENTROPY, 1) and abs(p.tau + 1.5) < 1e-7
+    assert (mtl.make_policy("conf").use_threshold, mtl.make_policy(1).score) == (0, 1)
+    mtl.dllm_masked_readout_destroy(h)
+
+
+def test_step_out_struct_matches_header():
+    """The ctypes struct lists the header's dllm_step_out fields in order."""
+    text = open(HEADER).read()
+    body = re.search(r"typedef struct \{([^}]*)\} dllm_step_out;", text).group(1)
+    fields = re.findall(r"\*\s*(\w+);", body)
+    assert fields == [f[0] for f in _abi.dllm_step_out._fields_]
+    body = re.search(r"typedef struct \{([^}]*)\} dllm_policy;", text).group(1)
+    assert re.findall(r"(\w+);", body) == [f[0] for f in _abi.dllm_policy._fields_]
 
 
 def test_step_without_device_reports_hip_error():
