@@ -2,6 +2,7 @@
 """Benchmark of the masked-token readout on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llada|tiny|dream|lc_low|lc_high]
+                    [--score conf|margin|neg_entropy] [--tau T]
 
 A step is one denoising readout (compaction, masked LM-head GEMM with the
 streaming vocabulary reduction, merge, top-k commit) over one synthetic
@@ -14,7 +15,10 @@ region).  All inputs are resident in HBM before timing starts.
 
 Prints ONE JSON line: masked tokens/s, the GEMM kernel's roofline (HIP
 events around its launch on the library's stream), and the fp64 CPU
-oracle timed on a bounded sample of the same workload.
+oracle timed on a bounded sample of the same workload.  ``--score`` and
+``--tau`` time another selection policy (ranking by top-2 margin or negative
+entropy, whose statistics the GEMM then also accumulates; threshold commits
+with cap k) instead of the default top-k by confidence.
 """
 from __future__ import annotations
 
@@ -76,16 +80,24 @@ def blas_threads() -> int:
         return 1
 
 
+def kernel_source_sha(kernel_src: str) -> str:
+    """sha256 over a GEMM kernel's source and the headers its code comes from."""
+    h = hashlib.sha256()
+    for f in (kernel_src, os.path.join(CSRC, "readout_internal.h"), os.path.join(CSRC, "online_state.h")):
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
 def traffic_from_profile(workload: str, kernel_src: str):
     """HBM bytes per GEMM launch from the committed rocprofv3 counter summary
     (profiles/<kernel>_<workload>_hbm_counters.md), or None when there is
-    none or the kernel's source file changed since the counters were taken."""
+    none or the kernel's sources changed since the counters were taken."""
     stem = os.path.splitext(os.path.basename(kernel_src))[0]
     path = os.path.join(ROOT, "profiles", f"{stem}_{workload}_hbm_counters.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
-    src = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
+    src = kernel_source_sha(kernel_src)
     m_sha = re.search(r"source sha256:\s*([0-9a-f]{64})", text)
     m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
     if not m_sha or not m_b or m_sha.group(1) != src:
@@ -134,6 +146,10 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="llada")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     ap.add_argument("--slices", type=int, default=0, help="force the GEMM's vocabulary slice count")
+    ap.add_argument("--score", choices=["conf", "margin", "neg_entropy"], default="conf",
+                    help="ranking score of the selection (default: confidence)")
+    ap.add_argument("--tau", type=float, default=None,
+                    help="threshold commits (score >= tau, at least 1, at most k) instead of top-k")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 3 times (reference for HBM byte counters)")
     args = ap.parse_args(argv)
@@ -202,7 +218,7 @@ def main(argv=None) -> int:
             a, b = ev[timed_index]
             mtl.dllm_masked_readout_set_gemm_events(rd.handle, a, b)
         out = {"m_out": m_slots.data_ptr() + 4 * i}
-        rd.step(Hts[t], mt, tt, cfg.k, lo, hi, cfg.block, out=out)
+        rd.step(Hts[t], mt, tt, cfg.k, lo, hi, cfg.block, out=out, score=args.score, tau=args.tau)
 
     for i in range(args.warmup):
         one(i, None)
@@ -224,11 +240,15 @@ def main(argv=None) -> int:
     peak_mem = int(torch.cuda.max_memory_allocated())
 
     d, V = cfg.d, cfg.V
+    ext = args.score != "conf"
     small = (min(cfg.block, hi - lo) if cfg.block else hi - lo) <= 32
     if small:
-        # HBM-bound: every launch streams all of W_lm once plus the gathered rows.
+        # HBM-bound: every launch streams all of W_lm once plus the gathered
+        # rows, and writes one partial record per (row, vocabulary slice):
+        # 16 B (max, argmax, sum), 24 B with the margin / entropy terms.
         slices = (V + 127) // 128
-        bytes_per = V * d * 2 + timed_M * d * 2 + timed_M * slices * 12 + timed_M * 4
+        rec_bytes = 24 if ext else 16
+        bytes_per = V * d * 2 + timed_M * d * 2 + timed_M * slices * rec_bytes + timed_M * 4
         achieved = float(bytes_per.sum()) / (gemm_ms.sum() * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4))
@@ -238,8 +258,9 @@ def main(argv=None) -> int:
         roof = dict(bound="mfma", achieved=round(achieved, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
                     frac=round(achieved / BF16_PEAK_TFLOPS, 4))
     src = os.path.join(CSRC, "gemm_online.hip" if small else "gemm_persistent.hip")
-    roof["traffic"] = traffic_from_profile(args.workload, src)
-    roof["kernel"] = "k_gemm_online<SmallTile>" if small else "k_gemm_persistent"
+    roof["traffic"] = None if ext else traffic_from_profile(args.workload, src)
+    roof["kernel"] = ("k_gemm_online<SmallTile, %s>" if small else "k_gemm_persistent<%s>") % (
+        "true" if ext else "false")
     roof["kernel_avg_us"] = round(float(gemm_ms.mean()) * 1e3, 2)
 
     value = masked_rows / elapsed
@@ -265,6 +286,7 @@ def main(argv=None) -> int:
             "full_logits_fp32_bytes": cfg.L * V * 4,
             "workspace_bytes": int(rd.workspace.numel()),
             "parallelism": "single GPU",
+            "policy": {"score": args.score, "threshold": args.tau},
         },
         "roofline": roof,
     }
