@@ -14,6 +14,7 @@ from .readout import (  # noqa: F401
     select_threshold,
     apply_updates,
     readout_step,
+    readout_step_batch,
     readout_rows,
     StepResult,
 )

@@ -209,3 +209,25 @@ def readout_step(H_bits: np.ndarray, W_bits: np.ndarray, mask: np.ndarray, token
     sel_tok = np.asarray([st["tok"][where[int(p)]] for p in sel], dtype=np.int32)
     t2, m2 = apply_updates(tokens, mask, sel, sel_tok)
     return StepResult(C, st, sel, sel_tok, t2, m2)
+
+
+def readout_step_batch(H_bits: np.ndarray, W_bits: np.ndarray, mask: np.ndarray, tokens: np.ndarray,
+                       seqs, block: int = 0, score: str = "conf", tau: float | None = None,
+                       row_chunk: int = 2048, W64: np.ndarray | None = None) -> list:
+    """B independent readout steps that share one LM head: sequence b has
+    hidden states H_bits[b] [L, d], mask[b], tokens[b] and its own
+    (k, win_lo, win_hi) = seqs[b]; ``block``, ``score`` and ``tau`` are common.
+
+    Serving many requests at once (Survey, Main Findings: microbatching;
+    "Real-world applications": high-throughput serving of concurrent
+    requests) changes how the work is scheduled, not what a step computes,
+    so each sequence's result is exactly readout_step on that sequence
+    alone.  Returns one StepResult per sequence."""
+    H_bits = np.asarray(H_bits)
+    if W64 is None:
+        W64 = widen_bf16(W_bits)
+    out = []
+    for b, (k, lo, hi) in enumerate(seqs):
+        out.append(readout_step(H_bits[b], W_bits, mask[b], tokens[b], int(k), int(lo), int(hi), block,
+                                score=score, tau=tau, row_chunk=row_chunk, W64=W64))
+    return out

@@ -398,3 +398,80 @@ def test_planted_rows_give_planted_tokens():
     assert np.median(st["gap2"]) > 6.0
     res = oracle.readout_step(inp.H, inp.W, inp.mask, inp.tokens, cfg.k)
     assert set(res.sel) <= set(P.rows)
+
+
+# ----------------------------------------------------------------- batched steps
+
+def _brute_step(H, W, mask, tokens, k, lo, hi, block):
+    """One step by brute force (exact logits, per-row scan, linear-scan
+    selection, commit), windows and blocks included."""
+    h, w = oracle.widen_bf16(H), oracle.widen_bf16(W)
+    masked = [i for i in range(lo, hi) if mask[i]]
+    if block > 0 and masked:
+        b_lo = lo + ((masked[0] - lo) // block) * block
+        masked = [i for i in masked if b_lo <= i < min(b_lo + block, hi)]
+    rows = {}
+    for i in masked:
+        z = [math.fsum(float(h[i, j]) * float(w[v, j]) for j in range(h.shape[1])) for v in range(w.shape[0])]
+        rows[i] = _brute_row(z)
+    sel = _linear_scan_topk([rows[i]["conf"] for i in masked], masked, k)
+    t2, m2 = tokens.copy(), mask.copy()
+    for i in sel:
+        t2[i] = rows[i]["tok"]
+        m2[i] = 0
+    return masked, sel, t2, m2
+
+
+def test_batch_against_brute_force_per_sequence():
+    """Each sequence of a batch gets exactly its own brute-force step: its own
+    hidden states, mask, tokens, k and window, never another sequence's."""
+    rng = np.random.default_rng(41)
+    B, L, d, V = 4, 40, 12, 30
+    H = _rand_bf16(rng, (B, L, d))
+    W = _rand_bf16(rng, (V, d), 0.3)
+    mask = (rng.random((B, L)) < 0.6).astype(np.uint8)
+    mask[2] = 0                                   # a sequence with nothing to do
+    tokens = rng.integers(0, V, size=(B, L)).astype(np.int32)
+    tokens[mask != 0] = V
+    seqs = [(3, 0, L), (5, 10, 30), (2, 0, L), (0, 0, L)]
+    for block in (0, 8):
+        res = oracle.readout_step_batch(H, W, mask, tokens, seqs, block)
+        assert len(res) == B
+        for b, (k, lo, hi) in enumerate(seqs):
+            cand, sel, t2, m2 = _brute_step(H[b], W, mask[b], tokens[b], k, lo, hi, block)
+            assert list(res[b].positions) == cand
+            assert list(res[b].sel) == sel
+            np.testing.assert_array_equal(res[b].tokens, t2)
+            np.testing.assert_array_equal(res[b].mask, m2)
+
+
+def test_batch_permutation_and_independence():
+    """Permuting the sequences permutes the results; changing one sequence's
+    inputs leaves every other sequence's result unchanged."""
+    rng = np.random.default_rng(43)
+    B, L, d, V = 5, 64, 16, 50
+    H = _rand_bf16(rng, (B, L, d))
+    W = _rand_bf16(rng, (V, d), 0.3)
+    mask = (rng.random((B, L)) < 0.5).astype(np.uint8)
+    tokens = np.full((B, L), V, np.int32)
+    seqs = [(int(rng.integers(1, 8)), 0, L) for _ in range(B)]
+    base = oracle.readout_step_batch(H, W, mask, tokens, seqs, score="margin")
+    perm = rng.permutation(B)
+    pr = oracle.readout_step_batch(H[perm], W, mask[perm], tokens[perm], [seqs[i] for i in perm], score="margin")
+    for j, i in enumerate(perm):
+        assert list(pr[j].sel) == list(base[i].sel)
+        np.testing.assert_array_equal(pr[j].tokens, base[i].tokens)
+    H2, m2 = H.copy(), mask.copy()
+    H2[3] = _rand_bf16(rng, (L, d))
+    m2[3] = 1
+    ch = oracle.readout_step_batch(H2, W, m2, tokens, seqs, score="margin")
+    for b in range(B):
+        if b != 3:
+            assert list(ch[b].sel) == list(base[b].sel)
+            np.testing.assert_array_equal(ch[b].stats["margin"], base[b].stats["margin"])
+    # identical sequences give identical results
+    Hs = np.repeat(H[:1], B, axis=0)
+    same = oracle.readout_step_batch(Hs, W, np.repeat(mask[:1], B, axis=0), np.repeat(tokens[:1], B, axis=0),
+                                     [seqs[0]] * B)
+    for b in range(1, B):
+        assert list(same[b].sel) == list(same[0].sel)

@@ -72,3 +72,20 @@ def test_plant_record():
     H0, _ = WL.hidden(WL.small_config(cfg, plant_frac=0.0))
     changed = np.flatnonzero(np.any(H != H0, axis=1))
     assert set(changed) <= set(P.rows)
+
+
+def test_batch_sequences_draw_their_own_bytes():
+    """Sequence 0 of a batch draws the bytes of the unbatched seeds; the other
+    sequences draw different, reproducible bytes."""
+    base = WL.WORKLOADS["llada_like_semi_ar_batch16"]
+    assert base.batch == 16 and base.win == (3072, 4096)
+    cfg = WL.small_config(base, L=64, d=128, V=300, batch=3, suffix=32)
+    H0 = WL.hidden(cfg, step=2)[0]
+    Hb = WL.hidden_batch(cfg, step=2)
+    assert Hb.shape == (3, 64, 128)
+    np.testing.assert_array_equal(Hb[0], H0)
+    assert WL.sha256(Hb[1]) != WL.sha256(Hb[0]) and WL.sha256(Hb[2]) != WL.sha256(Hb[1])
+    np.testing.assert_array_equal(WL.hidden_batch(cfg, step=2), Hb)
+    inp = WL.make_batch(cfg)
+    assert inp.mask.shape == (3, 64) and np.all(inp.mask[:, 32:] == 1) and np.all(inp.mask[:, :32] == 0)
+    assert WL.sha256(inp.tokens[1]) != WL.sha256(inp.tokens[0])

@@ -15,11 +15,18 @@ Workloads follow the masked diffusion LLM setting of the pages:
     Experiment / More Results: block-wise decoding with 32-token blocks
     needs logits only for the current block.
 
+  * Serving many requests at once (Accelerating Masked Diffusion Large
+    Language Models: A Survey of Efficient Inference Techniques, Main
+    Findings: microbatching; throughput-bound serving): a batch of B
+    sequences decoded together, sharing the LM head.
+
 Seeding: every tensor comes from
 ``np.random.Generator(PCG64(SeedSequence([0xD11A, config, stream, step, chunk])))``
-with streams 0 = W_lm, 1 = hidden, 2 = mask/tokens, 3 = plant.  Large tensors
-are drawn in fixed chunks of ``CHUNK`` elements, each with its own seed, so
-the bytes do not depend on how many threads draw them.
+with streams 0 = W_lm, 1 = hidden, 2 = mask/tokens, 3 = plant; sequence
+b > 0 of a batch appends b to that list (sequence 0 draws exactly the bytes of
+an unbatched workload).  Large tensors are drawn in fixed chunks of
+``CHUNK`` elements, each with its own seed, so the bytes do not depend on how
+many threads draw them.
 """
 from __future__ import annotations
 
@@ -48,6 +55,7 @@ class Config:
     ``block``: 0 = candidates are all masked rows of the window; >0 = only the
     masked rows of the lowest ``block``-aligned block that still holds one.
     ``plant_frac``: fraction of all L rows that carry a planted dominant token.
+    ``batch``: number of sequences decoded together (each of length L).
     """
     id: int
     name: str
@@ -63,6 +71,7 @@ class Config:
     rms_norm: bool = False
     plant_frac: float = 0.0
     plant_margin: float = 8.0
+    batch: int = 1
 
     @property
     def win(self) -> tuple[int, int]:
@@ -83,14 +92,18 @@ WORKLOADS: dict[str, Config] = {c.name: c for c in (
               mask_kind="exact", mask_ratio=0.1),
     Config(5, "long_ctx_high_mask", L=131072, d=4096, V=126464, k=1024,
            mask_kind="exact", mask_ratio=0.9, plant_frac=0.05),
+    Config(6, "llada_like_semi_ar_batch16", L=4096, d=4096, V=126464, k=2, steps=32,
+           mask_kind="suffix", suffix=1024, block=32, rms_norm=True, batch=16),
 )}
 
 MASK_TOKEN_OFFSET = 0   # masked positions hold token id V + this (outside the vocabulary)
 
 
-def _rng(config_id: int, stream: int, step: int = 0, chunk: int = 0) -> np.random.Generator:
-    return np.random.Generator(np.random.PCG64(
-        np.random.SeedSequence([SEED_ROOT, int(config_id), int(stream), int(step), int(chunk)])))
+def _rng(config_id: int, stream: int, step: int = 0, chunk: int = 0, seq: int = 0) -> np.random.Generator:
+    key = [SEED_ROOT, int(config_id), int(stream), int(step), int(chunk)]
+    if seq:
+        key.append(int(seq))
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(key)))
 
 
 def _threads() -> int:
@@ -117,7 +130,7 @@ def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
 
 
 def _normal_bf16(n_rows: int, n_cols: int, std: float, config_id: int, stream: int,
-                 step: int = 0, rms_norm: bool = False) -> np.ndarray:
+                 step: int = 0, rms_norm: bool = False, seq: int = 0) -> np.ndarray:
     """[n_rows, n_cols] uint16 bf16 bits of N(0, std) draws, chunk-seeded.
 
     With ``rms_norm`` each row is scaled by 1/sqrt(mean(row**2) + RMS_EPS) in
@@ -134,7 +147,7 @@ def _normal_bf16(n_rows: int, n_cols: int, std: float, config_id: int, stream: i
 
     def work(span):
         c, a, b = span
-        x = _rng(config_id, stream, step, c).standard_normal(b - a, dtype=np.float32)
+        x = _rng(config_id, stream, step, c, seq).standard_normal(b - a, dtype=np.float32)
         if rms_norm:
             x = x.reshape(-1, n_cols)
             ms = np.mean(x.astype(np.float64) ** 2, axis=1, keepdims=True).astype(np.float32)
@@ -156,12 +169,12 @@ def w_lm(cfg: Config) -> np.ndarray:
     return _normal_bf16(cfg.V, cfg.d, W_STD, cfg.id, STREAM_W)
 
 
-def initial_state(cfg: Config) -> tuple[np.ndarray, np.ndarray]:
-    """(mask u8 [L], tokens i32 [L]) before the first step.
+def initial_state(cfg: Config, seq: int = 0) -> tuple[np.ndarray, np.ndarray]:
+    """(mask u8 [L], tokens i32 [L]) of sequence ``seq`` before the first step.
 
     Masked positions hold token id V (outside the vocabulary); the others hold
     uniform draws from [0, V)."""
-    g = _rng(cfg.id, STREAM_MASK)
+    g = _rng(cfg.id, STREAM_MASK, seq=seq)
     L = cfg.L
     mask = np.zeros(L, dtype=np.uint8)
     if cfg.mask_kind == "bernoulli":
@@ -190,7 +203,7 @@ class Plant:
     tokens: np.ndarray    # int32 [P] planted token per row
 
 
-def hidden(cfg: Config, W_bits: np.ndarray | None = None, step: int = 0
+def hidden(cfg: Config, W_bits: np.ndarray | None = None, step: int = 0, seq: int = 0
            ) -> tuple[np.ndarray, Plant | None]:
     """Final hidden states [L, d] (bf16 bits) for one step, plus the plant record.
 
@@ -200,12 +213,12 @@ def hidden(cfg: Config, W_bits: np.ndarray | None = None, step: int = 0
     of its other V-1 logits, sigma * E[max of V-1 N(0,1)] with
     sigma = |r| * 0.02 (the spread of r . w_v under W_lm's distribution).
     This needs one d-long dot product per planted row, no logits."""
-    H = _normal_bf16(cfg.L, cfg.d, 1.0, cfg.id, STREAM_HIDDEN, step, rms_norm=cfg.rms_norm)
+    H = _normal_bf16(cfg.L, cfg.d, 1.0, cfg.id, STREAM_HIDDEN, step, rms_norm=cfg.rms_norm, seq=seq)
     if cfg.plant_frac <= 0.0:
         return H, None
     if W_bits is None:
         raise ValueError("planting needs W_lm")
-    g = _rng(cfg.id, STREAM_PLANT, step)
+    g = _rng(cfg.id, STREAM_PLANT, step, seq=seq)
     P = int(round(cfg.plant_frac * cfg.L))
     rows = np.sort(g.choice(cfg.L, size=P, replace=False)).astype(np.int64)
     toks = g.integers(0, cfg.V, size=P, dtype=np.int64).astype(np.int32)
@@ -239,6 +252,29 @@ def make(cfg_or_name, W_bits: np.ndarray | None = None) -> StepInputs:
     H, plant = hidden(cfg, W, 0)
     mask, tokens = initial_state(cfg)
     return StepInputs(cfg, W, H, mask, tokens, plant)
+
+
+@dataclass
+class BatchInputs:
+    cfg: Config
+    W: np.ndarray
+    H: np.ndarray         # [B, L, d] bf16 bits
+    mask: np.ndarray      # [B, L]
+    tokens: np.ndarray    # [B, L]
+
+
+def hidden_batch(cfg: Config, W_bits: np.ndarray | None = None, step: int = 0) -> np.ndarray:
+    """[B, L, d] hidden states of every sequence of a batch at one step."""
+    return np.stack([hidden(cfg, W_bits, step, seq=b)[0] for b in range(cfg.batch)])
+
+
+def make_batch(cfg_or_name, W_bits: np.ndarray | None = None) -> BatchInputs:
+    """All inputs of the first step of a batched workload."""
+    cfg = WORKLOADS[cfg_or_name] if isinstance(cfg_or_name, str) else cfg_or_name
+    W = w_lm(cfg) if W_bits is None else W_bits
+    states = [initial_state(cfg, b) for b in range(cfg.batch)]
+    return BatchInputs(cfg, W, hidden_batch(cfg, W, 0), np.stack([m for m, _ in states]),
+                       np.stack([t for _, t in states]))
 
 
 def sha256(a: np.ndarray) -> str:
