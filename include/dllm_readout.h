@@ -186,6 +186,41 @@ dllm_status dllm_masked_readout_step_ex(dllm_readout *h, const uint16_t *hidden,
                                         int64_t win_hi, int64_t block, const dllm_policy *policy,
                                         const dllm_step_out *out);
 
+/* Largest number of sequences one batched step takes. */
+#define DLLM_BATCH_MAX 128
+
+/* One sequence of a batched step (host struct). */
+typedef struct {
+  int32_t k;      /* unmask count of this sequence, 0 <= k <= k_max */
+  int32_t win_lo; /* candidate window [win_lo, win_hi) of this sequence, */
+  int32_t win_hi; /* 0 <= win_lo <= win_hi <= L                          */
+} dllm_seq;
+
+/*
+ * Batched readout step: B sequences of length L, decoded together, share one
+ * pass over W_lm (serving concurrent requests: Accelerating Masked Diffusion
+ * Large Language Models: A Survey of Efficient Inference Techniques, Main
+ * Findings, microbatching and throughput-bound serving).  Each sequence gets
+ * exactly the result of dllm_masked_readout_step_ex on it alone, with its own
+ * k and window; block and policy are common.
+ *   B          1 <= B <= DLLM_BATCH_MAX, and B * L <= L_max of the handle
+ *   hidden     [B, L, d] bf16 (16-byte aligned)
+ *   mask       [B, L] u8 in/out;  tokens [B, L] i32 in/out
+ *   seqs       host array [B]
+ *   block      as for dllm_masked_readout_step (>= 0)
+ *   policy     NULL = top-k by confidence
+ *   out        host struct of optional device outputs, now per sequence:
+ *              n_out, m_out [B]; sel_idx, sel_tok, sel_conf [B * k_max] with
+ *              sequence b at b * k_max; row_* [B * L] with sequence b at
+ *              b * L.  Positions are within the sequence (0 <= p < L).
+ * Errors as for dllm_masked_readout_step, checked for every sequence before
+ * anything is queued.
+ */
+dllm_status dllm_masked_readout_step_batch(dllm_readout *h, int32_t B, const uint16_t *hidden, int64_t L,
+                                           uint8_t *mask, int32_t *tokens, const dllm_seq *seqs,
+                                           int64_t block, const dllm_policy *policy,
+                                           const dllm_step_out *out);
+
 /* Free the host handle (no device memory is owned).  NULL -> DLLM_OK. */
 dllm_status dllm_masked_readout_destroy(dllm_readout *h);
 

@@ -12,6 +12,7 @@ memory and streams.
 from __future__ import annotations
 
 from ._abi import (  # noqa: F401
+    DLLM_BATCH_MAX,
     DLLM_ERR_HIP,
     DLLM_ERR_INVALID_ARG,
     DLLM_ERR_UNSUPPORTED,
@@ -29,9 +30,11 @@ from ._abi import (  # noqa: F401
     dllm_masked_readout_set_gemm_events,
     dllm_masked_readout_set_slices,
     dllm_masked_readout_step,
+    dllm_masked_readout_step_batch,
     dllm_masked_readout_step_ex,
     dllm_masked_readout_workspace_bytes,
     dllm_policy,
+    dllm_seq,
     dllm_status_string,
     load,
     make_policy,
@@ -103,6 +106,37 @@ class MaskedReadout:
                                              int(win_hi), int(block), make_policy(score, tau), out)
         if st != DLLM_OK:
             raise DllmError(st, "dllm_masked_readout_step")
+
+    def outputs_batch(self, B: int, L: int, ext: bool = False):
+        """Freshly allocated per-sequence output buffers for step_batch()."""
+        import torch
+        dev = self.W_lm.device
+        i32 = dict(dtype=torch.int32, device=dev)
+        f32 = dict(dtype=torch.float32, device=dev)
+        K = max(self.k_max, 1)
+        o = dict(n_out=torch.zeros(B, **i32), m_out=torch.zeros(B, **i32),
+                 sel_idx=torch.full((B, K), -1, **i32), sel_tok=torch.full((B, K), -1, **i32),
+                 sel_conf=torch.zeros((B, K), **f32), row_idx=torch.full((B, L), -1, **i32),
+                 row_tok=torch.full((B, L), -1, **i32), row_conf=torch.zeros((B, L), **f32),
+                 row_lse=torch.zeros((B, L), **f32))
+        if ext:
+            o["row_margin"] = torch.zeros((B, L), **f32)
+            o["row_entropy"] = torch.zeros((B, L), **f32)
+        return o
+
+    def step_batch(self, hidden, mask, tokens, seqs, block: int = 0, out: dict | None = None, score="conf",
+                   tau: float | None = None) -> None:
+        """Queue one batched step: ``hidden`` [B, L, d], ``mask``/``tokens``
+        [B, L], ``seqs`` B (k, win_lo, win_hi) triples.  Outputs (outputs_batch)
+        are per sequence; sel_* have a row stride of max(k_max, 1), which is
+        k_max for any handle that can commit."""
+        B, L = int(hidden.shape[0]), int(hidden.shape[1])
+        if len(seqs) != B:
+            raise ValueError("one (k, win_lo, win_hi) per sequence")
+        pol = None if (score == "conf" and tau is None) else make_policy(score, tau)
+        st = dllm_masked_readout_step_batch(self.handle, B, hidden, L, mask, tokens, seqs, int(block), pol, out)
+        if st != DLLM_OK:
+            raise DllmError(st, "dllm_masked_readout_step_batch")
 
     def close(self) -> None:
         if getattr(self, "handle", None):

@@ -19,6 +19,7 @@ DLLM_ERR_UNSUPPORTED = 2
 DLLM_ERR_WORKSPACE = 3
 DLLM_ERR_HIP = 4
 DLLM_K_MAX_LIMIT = 4096
+DLLM_BATCH_MAX = 128
 
 DLLM_SCORE_CONF = 0
 DLLM_SCORE_MARGIN = 1
@@ -30,6 +31,7 @@ EXPORTED = (
     "dllm_masked_readout_create",
     "dllm_masked_readout_step",
     "dllm_masked_readout_step_ex",
+    "dllm_masked_readout_step_batch",
     "dllm_masked_readout_destroy",
     "dllm_status_string",
     "dllm_masked_readout_set_slices",
@@ -50,6 +52,14 @@ class dllm_step_out(C.Structure):
         ("row_lse", C.c_void_p),
         ("row_margin", C.c_void_p),
         ("row_entropy", C.c_void_p),
+    ]
+
+
+class dllm_seq(C.Structure):
+    _fields_ = [
+        ("k", C.c_int32),
+        ("win_lo", C.c_int32),
+        ("win_hi", C.c_int32),
     ]
 
 
@@ -85,6 +95,10 @@ def load(path: str = LIB_PATH):
     lib.dllm_masked_readout_step_ex.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p,
                                                 C.c_int32, C.c_int64, C.c_int64, C.c_int64,
                                                 C.POINTER(dllm_policy), C.POINTER(dllm_step_out)]
+    lib.dllm_masked_readout_step_batch.restype = C.c_int
+    lib.dllm_masked_readout_step_batch.argtypes = [C.c_void_p, C.c_int32, C.c_void_p, C.c_int64, C.c_void_p,
+                                                   C.c_void_p, C.POINTER(dllm_seq), C.c_int64,
+                                                   C.POINTER(dllm_policy), C.POINTER(dllm_step_out)]
     lib.dllm_masked_readout_destroy.restype = C.c_int
     lib.dllm_masked_readout_destroy.argtypes = [C.c_void_p]
     lib.dllm_status_string.restype = C.c_char_p
@@ -164,6 +178,23 @@ def dllm_masked_readout_step_ex(handle, hidden, L: int, mask, tokens, k: int, wi
     return load().dllm_masked_readout_step_ex(handle, _ptr(hidden), L, _ptr(mask), _ptr(tokens), k, win_lo,
                                               win_hi, block, C.byref(policy) if policy is not None else None,
                                               C.byref(so) if so is not None else None)
+
+
+def dllm_masked_readout_step_batch(handle, B: int, hidden, L: int, mask, tokens, seqs, block: int = 0,
+                                   policy: dllm_policy | None = None, out: dict | None = None) -> int:
+    """``seqs``: B (k, win_lo, win_hi) triples (or a dllm_seq array)."""
+    if not isinstance(seqs, C.Array):
+        arr = (dllm_seq * max(len(seqs), 1))()
+        for i, (k, lo, hi) in enumerate(seqs):
+            arr[i] = dllm_seq(int(k), int(lo), int(hi))
+        seqs = arr
+    so = None
+    if out:
+        so = dllm_step_out(**{key: _ptr(v) for key, v in out.items()})
+    return load().dllm_masked_readout_step_batch(handle, int(B), _ptr(hidden), int(L), _ptr(mask), _ptr(tokens),
+                                                 seqs, int(block),
+                                                 C.byref(policy) if policy is not None else None,
+                                                 C.byref(so) if so is not None else None)
 
 
 def dllm_masked_readout_destroy(handle) -> int:

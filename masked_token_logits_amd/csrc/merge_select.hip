@@ -88,16 +88,47 @@ __global__ __launch_bounds__(kMergeWaves * 64) void k_merge(const int32_t* __res
 
 constexpr int kSelThreads = 1024;
 
+// One workgroup per sequence (a single sequence: one workgroup over all rows).
+// The sequence's rows are [start, start + M) of the compacted list; keys hold
+// the global row index, positions are idx[row] - pos_base within the sequence.
 __global__ __launch_bounds__(kSelThreads) void k_topk_scatter(
-    const int32_t* __restrict__ ctr, int k, Policy pol, const uint64_t* __restrict__ keys,
-    const int32_t* __restrict__ idx, const int32_t* __restrict__ row_tok, const float* __restrict__ row_conf,
-    uint8_t* __restrict__ mask, int32_t* __restrict__ tokens, int32_t* n_out, int32_t* m_out, int32_t* sel_idx,
-    int32_t* sel_tok, float* sel_conf) {
+    const int32_t* __restrict__ ctr, const int32_t* __restrict__ req, int64_t L, int k_stride, int k_single,
+    Policy pol, const uint64_t* __restrict__ keys, const int32_t* __restrict__ idx,
+    const int32_t* __restrict__ row_tok, const float* __restrict__ row_conf, const float* __restrict__ row_lse,
+    const float* __restrict__ row_margin, const float* __restrict__ row_entropy, uint8_t* __restrict__ mask,
+    int32_t* __restrict__ tokens, dllm_step_out o) {
   __shared__ uint32_t hist[256];
   __shared__ uint64_t sel[kTopkCap];
   __shared__ int s_digit, s_remaining, s_done, s_count;
   const int tid = threadIdx.x;
-  const int M = ctr[0];
+  const int b = blockIdx.x;
+  int start, M, k;
+  int64_t pos_base;
+  if (req) {
+    start = req[4 * b];
+    M = req[4 * b + 1];
+    k = req[4 * b + 2];
+    pos_base = (int64_t)b * L;
+  } else {
+    start = 0;
+    M = ctr[0];
+    k = k_single;
+    pos_base = 0;
+  }
+  const uint64_t* kb = keys + start;
+  if (req) {
+    // batched: this sequence's row outputs, from the merged workspace arrays
+    for (int i = tid; i < M; i += kSelThreads) {
+      const int r = start + i;
+      const size_t slot = (size_t)pos_base + (size_t)i;
+      if (o.row_idx) o.row_idx[slot] = (int32_t)(idx[r] - pos_base);
+      if (o.row_tok) o.row_tok[slot] = row_tok[r];
+      if (o.row_conf) o.row_conf[slot] = row_conf[r];
+      if (o.row_lse) o.row_lse[slot] = row_lse[r];
+      if (o.row_margin && row_margin) o.row_margin[slot] = row_margin[r];
+      if (o.row_entropy && row_entropy) o.row_entropy[slot] = row_entropy[r];
+    }
+  }
   int n = k < M ? k : M;
   if (pol.use_threshold && n > 0) {
     // rows whose score is >= tau: their key's high word is >= tau's pattern
@@ -105,7 +136,7 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_scatter(
     if (tid == 0) s_count = 0;
     __syncthreads();
     int c = 0;
-    for (int i = tid; i < M; i += kSelThreads) c += (uint32_t)(keys[i] >> 32) >= tk ? 1 : 0;
+    for (int i = tid; i < M; i += kSelThreads) c += (uint32_t)(kb[i] >> 32) >= tk ? 1 : 0;
     if (c) atomicAdd(&s_count, c);
     __syncthreads();
     const int cnt = s_count;
@@ -113,8 +144,8 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_scatter(
     n = cnt < 1 ? 1 : (cnt < n ? cnt : n);
   }
   if (tid == 0) {
-    if (n_out) *n_out = n;
-    if (m_out) *m_out = M;
+    if (o.n_out) o.n_out[b] = n;
+    if (o.m_out) o.m_out[b] = M;
   }
   if (n <= 0) return;
 
@@ -126,7 +157,7 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_scatter(
       for (int i = tid; i < 256; i += kSelThreads) hist[i] = 0;
       __syncthreads();
       for (int i = tid; i < M; i += kSelThreads) {
-        const uint64_t key = keys[i];
+        const uint64_t key = kb[i];
         if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
       }
       __syncthreads();
@@ -157,7 +188,7 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_scatter(
   if (tid == 0) s_count = 0;
   __syncthreads();
   for (int i = tid; i < M; i += kSelThreads) {
-    const uint64_t key = keys[i];
+    const uint64_t key = kb[i];
     if (key >= prefix) {
       const int slot = atomicAdd(&s_count, 1);
       if (slot < kTopkCap) sel[slot] = key;
@@ -186,17 +217,18 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_scatter(
       __syncthreads();
     }
   }
+  const size_t sbase = (size_t)b * (size_t)k_stride;
   for (int i = tid; i < n; i += kSelThreads) {
     const uint64_t key = sel[i];
     const int row = (int)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFu));
-    if (key == 0 || row < 0 || row >= M) continue;  // only reachable if fewer than n keys qualified
+    if (key == 0 || row < start || row >= start + M) continue;  // only reachable if fewer than n keys qualified
     const int pos = idx[row];
     const int tok = row_tok[row];
     tokens[pos] = tok;
     mask[pos] = 0;
-    if (sel_idx) sel_idx[i] = pos;
-    if (sel_tok) sel_tok[i] = tok;
-    if (sel_conf) sel_conf[i] = row_conf[row];
+    if (o.sel_idx) o.sel_idx[sbase + i] = (int32_t)(pos - pos_base);
+    if (o.sel_tok) o.sel_tok[sbase + i] = tok;
+    if (o.sel_conf) o.sel_conf[sbase + i] = row_conf[row];
   }
 }
 
@@ -204,18 +236,23 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_scatter(
 // merges every row's slices (16-byte (m, a, s, 0) records written by the
 // streaming GEMM into p.m, plus (m2, t) records in p.m2 for the extended
 // statistics; 32 lanes per row, loads issued U at a time so their
-// latencies overlap, then a butterfly), ranks the rows by counting (row r
-// precedes r' iff its score is larger, or equal with the lower row = lower
-// position) and commits the first n.
+// latencies overlap, then a butterfly), ranks each row among the rows of
+// its sequence by counting (row r precedes r' iff its score is larger, or
+// equal with the lower row = lower position) and commits each sequence's
+// first n.  A batched step (req != nullptr) has rows b * L + p.
 constexpr int kFinishThreads = 1024;
 static_assert(kFinishThreads == 32 * kSmallBM, "32 lanes per row");
+static_assert(kBatchMax <= kFinishThreads, "one thread per sequence");
 template <bool EXT>
 __global__ __launch_bounds__(kFinishThreads) void k_finish_small(const int32_t* __restrict__ ctr,
-                                                                const int32_t* __restrict__ idx, Partials p,
-                                                                Policy pol, int k, uint8_t* __restrict__ mask,
+                                                                const int32_t* __restrict__ idx,
+                                                                const int32_t* __restrict__ req, int B, int64_t L,
+                                                                int k_stride, Partials p, Policy pol, int k,
+                                                                uint8_t* __restrict__ mask,
                                                                 int32_t* __restrict__ tokens, dllm_step_out o) {
   __shared__ float s_conf[kSmallBM], s_lse[kSmallBM], s_score[kSmallBM], s_margin[kSmallBM], s_ent[kSmallBM];
-  __shared__ int s_tok[kSmallBM];
+  __shared__ int s_tok[kSmallBM], s_seq[kSmallBM];
+  __shared__ int s_n[kBatchMax];
   const int M = ctr[0];
   const int slices = ctr[3];
   const int r = threadIdx.x >> 5, sub = threadIdx.x & 31;
@@ -257,55 +294,68 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish_small(const int32_t* 
       s_ent[r] = f.entropy;
       s_score[r] = policy_score(f, pol.score) + 0.f;  // -0 -> +0
       s_tok[r] = st.a;
+      s_seq[r] = req ? (int)(idx[r] / L) : 0;
     }
   }
   __syncthreads();
-  int n = k < M ? k : M;
   const int t = threadIdx.x;
-  if (pol.use_threshold && n > 0) {
-    int cnt = 0;
-    for (int r2 = 0; r2 < M; ++r2) cnt += s_score[r2] >= pol.tau ? 1 : 0;
-    n = cnt < 1 ? 1 : (cnt < n ? cnt : n);
+  const int nseq = req ? B : 1;
+  if (t < nseq) {
+    const int Mb = req ? req[4 * t + 1] : M;
+    const int kb = req ? req[4 * t + 2] : k;
+    int n = kb < Mb ? kb : Mb;
+    if (pol.use_threshold && n > 0) {
+      int cnt = 0;
+      for (int r2 = 0; r2 < M; ++r2) cnt += (s_seq[r2] == t && s_score[r2] >= pol.tau) ? 1 : 0;
+      n = cnt < 1 ? 1 : (cnt < n ? cnt : n);
+    }
+    s_n[t] = n;
+    if (o.n_out) o.n_out[t] = n;
+    if (o.m_out) o.m_out[t] = Mb;
   }
+  __syncthreads();
   if (t < M) {
+    const int sq = s_seq[t];
     const float c = s_score[t];
     int rank = 0;
     for (int r2 = 0; r2 < M; ++r2) {
       const float c2 = s_score[r2];
-      rank += (c2 > c || (c2 == c && r2 < t)) ? 1 : 0;
+      rank += (s_seq[r2] == sq && (c2 > c || (c2 == c && r2 < t))) ? 1 : 0;
     }
-    const int pos = idx[t];
+    const int64_t pos_base = (int64_t)sq * L;     // 0 for a single sequence (sq == 0)
+    const int start = req ? req[4 * sq] : 0;
+    const size_t slot = req ? (size_t)pos_base + (size_t)(t - start) : (size_t)t;
+    const int g = idx[t];
+    const int pos = (int)(g - pos_base);
     const int tok = s_tok[t];
-    if (o.row_idx) o.row_idx[t] = pos;
-    if (o.row_tok) o.row_tok[t] = tok;
-    if (o.row_conf) o.row_conf[t] = s_conf[t];
-    if (o.row_lse) o.row_lse[t] = s_lse[t];
-    if (EXT && o.row_margin) o.row_margin[t] = s_margin[t];
-    if (EXT && o.row_entropy) o.row_entropy[t] = s_ent[t];
-    if (rank < n) {
-      tokens[pos] = tok;
-      mask[pos] = 0;
-      if (o.sel_idx) o.sel_idx[rank] = pos;
-      if (o.sel_tok) o.sel_tok[rank] = tok;
-      if (o.sel_conf) o.sel_conf[rank] = s_conf[t];
+    if (o.row_idx) o.row_idx[slot] = pos;
+    if (o.row_tok) o.row_tok[slot] = tok;
+    if (o.row_conf) o.row_conf[slot] = s_conf[t];
+    if (o.row_lse) o.row_lse[slot] = s_lse[t];
+    if (EXT && o.row_margin) o.row_margin[slot] = s_margin[t];
+    if (EXT && o.row_entropy) o.row_entropy[slot] = s_ent[t];
+    if (rank < s_n[sq]) {
+      tokens[g] = tok;
+      mask[g] = 0;
+      const size_t sb = (size_t)sq * (size_t)k_stride + (size_t)rank;
+      if (o.sel_idx) o.sel_idx[sb] = pos;
+      if (o.sel_tok) o.sel_tok[sb] = tok;
+      if (o.sel_conf) o.sel_conf[sb] = s_conf[t];
     }
-  }
-  if (t == 0) {
-    if (o.n_out) *o.n_out = n;
-    if (o.m_out) *o.m_out = M;
   }
 }
 
 }  // namespace
 
-hipError_t launch_finish_small(const int32_t* ctr, const int32_t* idx, Partials p, Policy pol, int k,
-                               uint8_t* mask, int32_t* tokens, dllm_step_out out, hipStream_t stream) {
+hipError_t launch_finish_small(const int32_t* ctr, const int32_t* idx, const int32_t* req, int B, int64_t L,
+                               int k_stride, Partials p, Policy pol, int k, uint8_t* mask, int32_t* tokens,
+                               dllm_step_out out, hipStream_t stream) {
   if (p.ext)
-    hipLaunchKernelGGL(k_finish_small<true>, dim3(1), dim3(kFinishThreads), 0, stream, ctr, idx, p, pol, k, mask,
-                       tokens, out);
+    hipLaunchKernelGGL(k_finish_small<true>, dim3(1), dim3(kFinishThreads), 0, stream, ctr, idx, req, B, L, k_stride,
+                       p, pol, k, mask, tokens, out);
   else
-    hipLaunchKernelGGL(k_finish_small<false>, dim3(1), dim3(kFinishThreads), 0, stream, ctr, idx, p, pol, k, mask,
-                       tokens, out);
+    hipLaunchKernelGGL(k_finish_small<false>, dim3(1), dim3(kFinishThreads), 0, stream, ctr, idx, req, B, L,
+                       k_stride, p, pol, k, mask, tokens, out);
   return hipGetLastError();
 }
 
@@ -323,12 +373,12 @@ hipError_t launch_merge(const int32_t* ctr, const int32_t* idx, Partials p, int 
   return hipGetLastError();
 }
 
-hipError_t launch_topk_scatter(const int32_t* ctr, int k, Policy pol, const uint64_t* keys, const int32_t* idx,
-                               const int32_t* row_tok, const float* row_conf, uint8_t* mask, int32_t* tokens,
-                               int32_t* n_out, int32_t* m_out, int32_t* sel_idx, int32_t* sel_tok,
-                               float* sel_conf, hipStream_t stream) {
-  hipLaunchKernelGGL(k_topk_scatter, dim3(1), dim3(kSelThreads), 0, stream, ctr, k, pol, keys, idx, row_tok,
-                     row_conf, mask, tokens, n_out, m_out, sel_idx, sel_tok, sel_conf);
+hipError_t launch_topk_scatter(const int32_t* ctr, const int32_t* req, int B, int64_t L, int k_stride, int k,
+                               Policy pol, const Workspace& ws, uint8_t* mask, int32_t* tokens,
+                               const dllm_step_out& out, hipStream_t stream) {
+  const int grid = req ? B : 1;
+  hipLaunchKernelGGL(k_topk_scatter, dim3(grid), dim3(kSelThreads), 0, stream, ctr, req, L, k_stride, k, pol, ws.keys,
+                     ws.idx, ws.row_tok, ws.row_conf, ws.row_lse, ws.row_margin, ws.row_entropy, mask, tokens, out);
   return hipGetLastError();
 }
 

@@ -63,6 +63,9 @@ size_t carve(int64_t L_max, int64_t V, uint8_t* base, dllm::Workspace* ws) {
   w.row_conf = reinterpret_cast<float*>(take(sizeof(float) * (size_t)L_max));
   w.row_lse = reinterpret_cast<float*>(take(sizeof(float) * (size_t)L_max));
   w.keys = reinterpret_cast<uint64_t*>(take(sizeof(uint64_t) * (size_t)L_max));
+  w.row_margin = reinterpret_cast<float*>(take(sizeof(float) * (size_t)L_max));
+  w.row_entropy = reinterpret_cast<float*>(take(sizeof(float) * (size_t)L_max));
+  w.req = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * 4 * (size_t)dllm::kBatchMax));
   w.part_cap = part_cap;
   if (ws) *ws = w;
   return off;
@@ -79,6 +82,140 @@ int choose_large_slices(int n_row_tiles, int64_t V, int cus) {
   if (s > dllm::kMaxLargeSlices) s = dllm::kMaxLargeSlices;
   if (s > n_vt) s = n_vt;
   return (int)s;
+}
+
+dllm_status parse_policy(const dllm_policy* policy, dllm::Policy* pol) {
+  *pol = {DLLM_SCORE_CONF, 0, 0.f};
+  if (!policy) return DLLM_OK;
+  if (policy->score < DLLM_SCORE_CONF || policy->score > DLLM_SCORE_NEG_ENTROPY) return DLLM_ERR_INVALID_ARG;
+  if (policy->use_threshold != 0 && policy->use_threshold != 1) return DLLM_ERR_INVALID_ARG;
+  if (policy->tau != policy->tau) return DLLM_ERR_INVALID_ARG;  // NaN
+  pol->score = policy->score;
+  pol->use_threshold = policy->use_threshold;
+  pol->tau = policy->tau + 0.f;  // -0 -> +0: the kernels compare order-preserving bit patterns
+  return DLLM_OK;
+}
+
+dllm_status ensure_device(dllm_readout* h) {
+  if (h->cus > 0) return DLLM_OK;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return DLLM_ERR_HIP;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return DLLM_ERR_HIP;
+  h->cus = cus;
+  return DLLM_OK;
+}
+
+// One validated step, single sequence (seqs == nullptr: k, win_lo, win_hi)
+// or batched (B sequences of length L, rows b * L + p).
+struct StepArgs {
+  const uint16_t* hidden;
+  int64_t L;
+  uint8_t* mask;
+  int32_t* tokens;
+  int64_t block;
+  int k;
+  int64_t win_lo, win_hi;
+  const dllm::SeqTable* seqs;
+  int B;
+  int64_t rows_max;     // host bound on the candidate rows of the step
+  int64_t hidden_rows;  // rows of the hidden tensor (L or B * L)
+};
+
+dllm_status run_step(dllm_readout* h, const StepArgs& a, const dllm::Policy& pol, const dllm_step_out& o) {
+  const dllm_status ds = ensure_device(h);
+  if (ds != DLLM_OK) return ds;
+  const dllm::Workspace& w = h->ws;
+  const bool batched = a.seqs != nullptr;
+  // margin / entropy are needed for ranking or output: keep (m2, t) too
+  const bool ext = pol.score != DLLM_SCORE_CONF || o.row_margin != nullptr || o.row_entropy != nullptr;
+  const dllm::Partials parts = {w.part_m, w.part_a, w.part_s, w.part_m2, w.part_t, ext};
+  const int64_t rows_max = a.rows_max;
+  const int V = (int)h->V, d = (int)h->d;
+  hipStream_t st = h->stream;
+
+  // Choose the GEMM variant from the host-known bound on M; the slice count
+  // of the persistent variant is fixed on the device once M is known.  The
+  // persistent kernel addresses hidden rows with 32-bit byte offsets, so it
+  // needs the hidden tensor to span less than 4 GiB.
+  enum { kSmall, kPersistent, kStreaming } path;
+  const int64_t n_vt_large = (h->V + dllm::kLargeBN - 1) / dllm::kLargeBN;
+  const bool offsets32 = a.hidden_rows * h->d * 2 < ((int64_t)1 << 32);
+  dllm::PlanParams plan = {};
+  int n_rt = 0;
+  if (rows_max <= dllm::kSmallBM) {
+    path = kSmall;
+    plan.fixed_slices = (int)small_slice_count(h->V);
+    plan.tile_rows = dllm::kSmallBM;
+  } else if (h->d % dllm::kPersistBK == 0 && offsets32) {
+    path = kPersistent;
+    int so = h->slices_override;
+    if (so > n_vt_large) so = (int)n_vt_large;
+    plan.fixed_slices = so;
+    plan.tile_rows = dllm::kPersistBM;
+    plan.n_vt = (int)n_vt_large;
+    plan.grid = h->cus;
+    plan.max_slices = 1024;
+    plan.part_cap = w.part_cap;
+  } else {
+    path = kStreaming;
+    n_rt = (int)((rows_max + dllm::kLargeBM - 1) / dllm::kLargeBM);
+    int sl = h->slices_override > 0 ? h->slices_override : choose_large_slices(n_rt, h->V, h->cus);
+    if (sl > n_vt_large) sl = (int)n_vt_large;
+    plan.fixed_slices = sl;
+    plan.tile_rows = dllm::kLargeBM;
+  }
+  hipError_t ce;
+  if (batched)
+    ce = dllm::launch_mask_compact_batch(a.mask, a.B, a.L, *a.seqs, a.block, plan, w.idx, w.ctr, w.req, st);
+  else if (path == kSmall)
+    ce = dllm::launch_mask_compact_small(a.mask, a.win_lo, a.win_hi, a.block, plan.fixed_slices, w.idx, w.ctr, st);
+  else
+    ce = dllm::launch_mask_compact(a.mask, a.win_lo, a.win_hi, a.block, plan, w.idx, w.ctr, st);
+  if (ce != hipSuccess) return DLLM_ERR_HIP;
+
+  const int32_t* req = batched ? w.req : nullptr;
+  const int k_stride = h->k_max;
+  if (rows_max > 0) {
+    hipError_t e;
+    if (h->ev_before && hipEventRecord(h->ev_before, st) != hipSuccess) return DLLM_ERR_HIP;
+    if (path == kSmall) {
+      e = dllm::launch_gemm_small(h->W, a.hidden, d, V, w.idx, w.ctr, plan.fixed_slices, parts, st);
+    } else if (path == kPersistent) {
+      e = dllm::launch_gemm_persistent(h->W, a.hidden, d, V, w.idx, w.ctr, h->cus, parts, st);
+    } else {
+      e = dllm::launch_gemm_large(h->W, a.hidden, d, V, w.idx, w.ctr, n_rt, plan.fixed_slices, parts, st);
+    }
+    if (h->log)
+      fprintf(stderr, "[dllm] step B=%d rows<=%lld path=%s slices=%d cus=%d ext=%d score=%d threshold=%d\n",
+              batched ? a.B : 0, (long long)rows_max,
+              path == kSmall ? "small" : path == kPersistent ? "persistent" : "streaming", plan.fixed_slices, h->cus,
+              (int)ext, pol.score, pol.use_threshold);
+    if (e != hipSuccess) return DLLM_ERR_HIP;
+    if (h->ev_after && hipEventRecord(h->ev_after, st) != hipSuccess) return DLLM_ERR_HIP;
+    if (path == kSmall) {
+      // merge, selection and commit of <= 32 rows in one workgroup
+      if (dllm::launch_finish_small(w.ctr, w.idx, req, a.B, a.L, k_stride, parts, pol, a.k, a.mask, a.tokens, o,
+                                    st) != hipSuccess)
+        return DLLM_ERR_HIP;
+      return DLLM_OK;
+    }
+    // single sequence: the merge writes the row outputs; batched: it fills
+    // the workspace rows and the selection copies each sequence's rows out
+    dllm_step_out om = {};
+    if (batched) {
+      om.row_margin = w.row_margin;
+      om.row_entropy = w.row_entropy;
+    } else {
+      om = o;
+    }
+    if (dllm::launch_merge(w.ctr, w.idx, parts, pol.score, (int)rows_max, w.row_tok, w.row_conf, w.row_lse,
+                           w.keys, om, st) != hipSuccess)
+      return DLLM_ERR_HIP;
+  }
+  if (dllm::launch_topk_scatter(w.ctr, req, a.B, a.L, k_stride, a.k, pol, w, a.mask, a.tokens, o, st) != hipSuccess)
+    return DLLM_ERR_HIP;
+  return DLLM_OK;
 }
 
 }  // namespace
@@ -160,15 +297,9 @@ dllm_status dllm_masked_readout_step_ex(dllm_readout* h, const uint16_t* hidden,
                                         int32_t* tokens, int32_t k, int64_t win_lo, int64_t win_hi,
                                         int64_t block, const dllm_policy* policy, const dllm_step_out* out) {
   if (!h || !hidden || !mask || !tokens) return DLLM_ERR_INVALID_ARG;
-  dllm::Policy pol = {DLLM_SCORE_CONF, 0, 0.f};
-  if (policy) {
-    if (policy->score < DLLM_SCORE_CONF || policy->score > DLLM_SCORE_NEG_ENTROPY) return DLLM_ERR_INVALID_ARG;
-    if (policy->use_threshold != 0 && policy->use_threshold != 1) return DLLM_ERR_INVALID_ARG;
-    if (policy->tau != policy->tau) return DLLM_ERR_INVALID_ARG;  // NaN
-    pol.score = policy->score;
-    pol.use_threshold = policy->use_threshold;
-    pol.tau = policy->tau + 0.f;  // -0 -> +0: the kernels compare order-preserving bit patterns
-  }
+  dllm::Policy pol;
+  const dllm_status ps = parse_policy(policy, &pol);
+  if (ps != DLLM_OK) return ps;
   if (L <= 0 || L > h->L_max) return DLLM_ERR_INVALID_ARG;
   if (k < 0 || k > h->k_max) return DLLM_ERR_INVALID_ARG;
   if (win_lo < 0 || win_lo > win_hi || win_hi > L) return DLLM_ERR_INVALID_ARG;
@@ -176,87 +307,61 @@ dllm_status dllm_masked_readout_step_ex(dllm_readout* h, const uint16_t* hidden,
   if (!aligned16(hidden)) return DLLM_ERR_UNSUPPORTED;
   dllm_step_out o = {};
   if (out) o = *out;
-  if (h->cus <= 0) {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return DLLM_ERR_HIP;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-      return DLLM_ERR_HIP;
-    h->cus = cus;
-  }
-
-  const dllm::Workspace& w = h->ws;
-  // margin / entropy are needed for ranking or output: keep (m2, t) too
-  const bool ext = pol.score != DLLM_SCORE_CONF || o.row_margin != nullptr || o.row_entropy != nullptr;
-  const dllm::Partials parts = {w.part_m, w.part_a, w.part_s, w.part_m2, w.part_t, ext};
   const int64_t span = win_hi - win_lo;
-  const int64_t rows_max = (block > 0 && block < span) ? block : span;  // upper bound on M
-  const int V = (int)h->V, d = (int)h->d;
-  hipStream_t st = h->stream;
+  StepArgs a = {};
+  a.hidden = hidden;
+  a.L = L;
+  a.mask = mask;
+  a.tokens = tokens;
+  a.block = block;
+  a.k = k;
+  a.win_lo = win_lo;
+  a.win_hi = win_hi;
+  a.seqs = nullptr;
+  a.B = 1;
+  a.rows_max = (block > 0 && block < span) ? block : span;
+  a.hidden_rows = L;
+  return run_step(h, a, pol, o);
+}
 
-  // Choose the GEMM variant from the host-known bound on M; the slice count
-  // of the persistent variant is fixed on the device once M is known.
-  enum { kSmall, kPersistent, kStreaming } path;
-  const int64_t n_vt_large = (h->V + dllm::kLargeBN - 1) / dllm::kLargeBN;
-  dllm::PlanParams plan = {};
-  int n_rt = 0;
-  if (rows_max <= dllm::kSmallBM) {
-    path = kSmall;
-    plan.fixed_slices = (int)small_slice_count(h->V);
-    plan.tile_rows = dllm::kSmallBM;
-  } else if (h->d % dllm::kPersistBK == 0) {
-    path = kPersistent;
-    int so = h->slices_override;
-    if (so > n_vt_large) so = (int)n_vt_large;
-    plan.fixed_slices = so;
-    plan.tile_rows = dllm::kPersistBM;
-    plan.n_vt = (int)n_vt_large;
-    plan.grid = h->cus;
-    plan.max_slices = 1024;
-    plan.part_cap = w.part_cap;
-  } else {
-    path = kStreaming;
-    n_rt = (int)((rows_max + dllm::kLargeBM - 1) / dllm::kLargeBM);
-    int sl = h->slices_override > 0 ? h->slices_override : choose_large_slices(n_rt, h->V, h->cus);
-    if (sl > n_vt_large) sl = (int)n_vt_large;
-    plan.fixed_slices = sl;
-    plan.tile_rows = dllm::kLargeBM;
+dllm_status dllm_masked_readout_step_batch(dllm_readout* h, int32_t B, const uint16_t* hidden, int64_t L,
+                                           uint8_t* mask, int32_t* tokens, const dllm_seq* seqs, int64_t block,
+                                           const dllm_policy* policy, const dllm_step_out* out) {
+  if (!h || !hidden || !mask || !tokens || !seqs) return DLLM_ERR_INVALID_ARG;
+  dllm::Policy pol;
+  const dllm_status ps = parse_policy(policy, &pol);
+  if (ps != DLLM_OK) return ps;
+  if (B < 1 || B > dllm::kBatchMax) return DLLM_ERR_INVALID_ARG;
+  if (L <= 0 || L > h->L_max || (int64_t)B * L > h->L_max) return DLLM_ERR_INVALID_ARG;
+  if (block < 0) return DLLM_ERR_INVALID_ARG;
+  dllm::SeqTable tab;
+  int64_t rows_max = 0;
+  for (int b = 0; b < B; ++b) {
+    const dllm_seq& q = seqs[b];
+    if (q.k < 0 || q.k > h->k_max) return DLLM_ERR_INVALID_ARG;
+    if (q.win_lo < 0 || q.win_lo > q.win_hi || (int64_t)q.win_hi > L) return DLLM_ERR_INVALID_ARG;
+    const int64_t span = (int64_t)q.win_hi - q.win_lo;
+    rows_max += (block > 0 && block < span) ? block : span;
+    tab.lo[b] = q.win_lo;
+    tab.hi[b] = q.win_hi;
+    tab.k[b] = q.k;
   }
-  const hipError_t ce = (path == kSmall)
-                            ? dllm::launch_mask_compact_small(mask, win_lo, win_hi, block, plan.fixed_slices, w.idx,
-                                                              w.ctr, st)
-                            : dllm::launch_mask_compact(mask, win_lo, win_hi, block, plan, w.idx, w.ctr, st);
-  if (ce != hipSuccess) return DLLM_ERR_HIP;
-
-  if (rows_max > 0) {
-    hipError_t e;
-    if (h->ev_before && hipEventRecord(h->ev_before, st) != hipSuccess) return DLLM_ERR_HIP;
-    if (path == kSmall) {
-      e = dllm::launch_gemm_small(h->W, hidden, d, V, w.idx, w.ctr, plan.fixed_slices, parts, st);
-    } else if (path == kPersistent) {
-      e = dllm::launch_gemm_persistent(h->W, hidden, d, V, w.idx, w.ctr, h->cus, parts, st);
-    } else {
-      e = dllm::launch_gemm_large(h->W, hidden, d, V, w.idx, w.ctr, n_rt, plan.fixed_slices, parts, st);
-    }
-    if (h->log)
-      fprintf(stderr, "[dllm] step rows<=%lld path=%s slices=%d cus=%d ext=%d score=%d threshold=%d\n",
-              (long long)rows_max, path == kSmall ? "small" : path == kPersistent ? "persistent" : "streaming",
-              plan.fixed_slices, h->cus, (int)ext, pol.score, pol.use_threshold);
-    if (e != hipSuccess) return DLLM_ERR_HIP;
-    if (h->ev_after && hipEventRecord(h->ev_after, st) != hipSuccess) return DLLM_ERR_HIP;
-    if (path == kSmall) {
-      // merge, selection and commit of <= 32 rows in one workgroup
-      if (dllm::launch_finish_small(w.ctr, w.idx, parts, pol, k, mask, tokens, o, st) != hipSuccess)
-        return DLLM_ERR_HIP;
-      return DLLM_OK;
-    }
-    if (dllm::launch_merge(w.ctr, w.idx, parts, pol.score, (int)rows_max, w.row_tok, w.row_conf, w.row_lse,
-                           w.keys, o, st) != hipSuccess)
-      return DLLM_ERR_HIP;
-  }
-  if (dllm::launch_topk_scatter(w.ctr, k, pol, w.keys, w.idx, w.row_tok, w.row_conf, mask, tokens, o.n_out,
-                                o.m_out, o.sel_idx, o.sel_tok, o.sel_conf, st) != hipSuccess)
-    return DLLM_ERR_HIP;
-  return DLLM_OK;
+  for (int b = B; b < dllm::kBatchMax; ++b) tab.lo[b] = tab.hi[b] = tab.k[b] = 0;
+  if (!aligned16(hidden)) return DLLM_ERR_UNSUPPORTED;
+  dllm_step_out o = {};
+  if (out) o = *out;
+  StepArgs a = {};
+  a.hidden = hidden;
+  a.L = L;
+  a.mask = mask;
+  a.tokens = tokens;
+  a.block = block;
+  a.k = 0;
+  a.seqs = &tab;
+  a.B = B;
+  a.rows_max = rows_max;
+  a.hidden_rows = (int64_t)B * L;
+  return run_step(h, a, pol, o);
 }
 
 }  // extern "C"

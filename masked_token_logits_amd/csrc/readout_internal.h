@@ -23,7 +23,18 @@ struct Workspace {
   float* row_conf;     // [L_max]   merged confidence
   float* row_lse;      // [L_max]   merged log-sum-exp
   uint64_t* keys;      // [L_max]   selection key: ordered score bits << 32 | (0xFFFFFFFF - row)
+  float* row_margin;   // [L_max]   merged margin (batched steps with the extended statistics)
+  float* row_entropy;  // [L_max]   merged entropy (same)
+  int32_t* req;        // [4 * kBatchMax] per sequence of a batched step: first row, M, k, 0
   int64_t part_cap;
+};
+
+constexpr int kBatchMax = DLLM_BATCH_MAX;
+
+// The sequences of a batched step, passed by value to the compaction kernel
+// (1.5 KiB of kernel arguments), which records them in Workspace::req.
+struct SeqTable {
+  int32_t lo[kBatchMax], hi[kBatchMax], k[kBatchMax];
 };
 
 // Partials of one step: (m, a, s) always, (m2, t) when `ext` (margin or
@@ -71,6 +82,11 @@ struct PlanParams {
 hipError_t launch_mask_compact(const uint8_t* mask, int64_t win_lo, int64_t win_hi, int64_t block,
                                PlanParams plan, int32_t* idx, int32_t* ctr, hipStream_t stream);
 
+// Batched: B windows, one per sequence of length L (rows are b * L + p);
+// writes Workspace::req and the plan for the total M.
+hipError_t launch_mask_compact_batch(const uint8_t* mask, int B, int64_t L, const SeqTable& seqs, int64_t block,
+                                     PlanParams plan, int32_t* idx, int32_t* ctr, int32_t* req, hipStream_t stream);
+
 // The same for windows that hold at most 32 candidates (one wave).
 hipError_t launch_mask_compact_small(const uint8_t* mask, int64_t win_lo, int64_t win_hi, int64_t block,
                                      int fixed_slices, int32_t* idx, int32_t* ctr, hipStream_t stream);
@@ -89,16 +105,22 @@ hipError_t launch_gemm_small(const uint16_t* W, const uint16_t* H, int d, int V,
 
 // Merge + selection + commit for at most kSmallBM candidate rows, in one
 // workgroup (replaces launch_merge + launch_topk_scatter on the small path).
-hipError_t launch_finish_small(const int32_t* ctr, const int32_t* idx, Partials p, Policy pol, int k,
-                               uint8_t* mask, int32_t* tokens, dllm_step_out out, hipStream_t stream);
+// Batched (req != nullptr): B sequences of length L, each ranked on its own;
+// outputs per sequence at b * k_stride (selection) and b * L (rows).
+hipError_t launch_finish_small(const int32_t* ctr, const int32_t* idx, const int32_t* req, int B, int64_t L,
+                               int k_stride, Partials p, Policy pol, int k, uint8_t* mask, int32_t* tokens,
+                               dllm_step_out out, hipStream_t stream);
 
 hipError_t launch_merge(const int32_t* ctr, const int32_t* idx, Partials p, int score, int max_rows,
                         int32_t* row_tok, float* row_conf, float* row_lse, uint64_t* keys,
                         const dllm_step_out& out, hipStream_t stream);
 
-hipError_t launch_topk_scatter(const int32_t* ctr, int k, Policy pol, const uint64_t* keys, const int32_t* idx,
-                               const int32_t* row_tok, const float* row_conf, uint8_t* mask, int32_t* tokens,
-                               int32_t* n_out, int32_t* m_out, int32_t* sel_idx, int32_t* sel_tok,
-                               float* sel_conf, hipStream_t stream);
+// Selection + commit.  Single sequence (req == nullptr): one workgroup over
+// all M rows, k as given; the merge already wrote the row outputs.
+// Batched: one workgroup per sequence over its rows (Workspace::req), which
+// also copies the sequence's row outputs from the workspace arrays.
+hipError_t launch_topk_scatter(const int32_t* ctr, const int32_t* req, int B, int64_t L, int k_stride, int k,
+                               Policy pol, const Workspace& ws, uint8_t* mask, int32_t* tokens,
+                               const dllm_step_out& out, hipStream_t stream);
 
 }  // namespace dllm

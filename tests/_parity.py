@@ -178,3 +178,26 @@ def check_commit(before_mask, before_tok, res, lo=0, hi=None):
     np.testing.assert_array_equal(after_tok[sel], res["sel_tok"])
     if hi is not None:
         assert np.all((sel >= lo) & (sel < hi))
+
+
+def run_batch(rd, Ht, mt, tt, seqs, block=0, score="conf", tau=None, ext=False):
+    """One batched step through the C ABI; returns one result dict per
+    sequence, shaped like run_step's."""
+    import torch
+    B, L = int(Ht.shape[0]), int(Ht.shape[1])
+    out = rd.outputs_batch(B, L, ext=ext)
+    rd.step_batch(Ht, mt, tt, seqs, block, out=out, score=score, tau=tau)
+    torch.cuda.synchronize()
+    host = {key: v.cpu().numpy() for key, v in out.items()}
+    mask, tokens = mt.cpu().numpy(), tt.cpu().numpy()
+    res = []
+    for b in range(B):
+        n, M = int(host["n_out"][b]), int(host["m_out"][b])
+        r = dict(n=n, M=M, mask=mask[b], tokens=tokens[b])
+        for key in ("sel_idx", "sel_tok", "sel_conf"):
+            r[key] = host[key][b, :n]
+        for key in ("row_idx", "row_tok", "row_conf", "row_lse", "row_margin", "row_entropy"):
+            if key in host:
+                r[key] = host[key][b, :M]
+        res.append(r)
+    return res

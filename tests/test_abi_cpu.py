@@ -140,6 +140,36 @@ def test_step_ex_policy_validation_before_any_hip_call():
     mtl.dllm_masked_readout_destroy(h)
 
 
+def test_step_batch_validation_before_any_hip_call():
+    st, h = _create()            # L_max = 512, k_max = 16
+    assert st == mtl.DLLM_OK
+    E = mtl
+    H, Mk, T = FAKE + 0x200000, FAKE + 0x300000, FAKE + 0x400000
+
+    def step(B=2, L=200, seqs=((4, 0, 200), (2, 10, 50)), block=0, hidden=H, policy=None):
+        return mtl.dllm_masked_readout_step_batch(h, B, hidden, L, Mk, T, list(seqs), block, policy)
+
+    assert step(B=0, seqs=()) == E.DLLM_ERR_INVALID_ARG
+    assert step(B=E.DLLM_BATCH_MAX + 1, L=1, seqs=[(0, 0, 1)] * (E.DLLM_BATCH_MAX + 1)) == E.DLLM_ERR_INVALID_ARG
+    assert step(L=0, seqs=((0, 0, 0), (0, 0, 0))) == E.DLLM_ERR_INVALID_ARG
+    assert step(B=3, L=200, seqs=((1, 0, 1),) * 3) == E.DLLM_ERR_INVALID_ARG     # 3 * 200 > L_max
+    assert step(seqs=((17, 0, 200), (1, 0, 1))) == E.DLLM_ERR_INVALID_ARG        # k > k_max
+    assert step(seqs=((-1, 0, 200), (1, 0, 1))) == E.DLLM_ERR_INVALID_ARG
+    assert step(seqs=((1, 0, 201), (1, 0, 1))) == E.DLLM_ERR_INVALID_ARG         # window past L
+    assert step(seqs=((1, 5, 4), (1, 0, 1))) == E.DLLM_ERR_INVALID_ARG
+    assert step(seqs=((1, 0, 10), (1, -1, 1))) == E.DLLM_ERR_INVALID_ARG
+    assert step(block=-1) == E.DLLM_ERR_INVALID_ARG
+    assert step(hidden=H + 2) == E.DLLM_ERR_UNSUPPORTED
+    assert step(policy=_abi.dllm_policy(7, 0, 0.0)) == E.DLLM_ERR_INVALID_ARG
+    assert mtl.dllm_masked_readout_step_batch(None, 1, H, 10, Mk, T, [(1, 0, 10)]) == E.DLLM_ERR_INVALID_ARG
+    assert mtl.dllm_masked_readout_step_batch(h, 1, None, 10, Mk, T, [(1, 0, 10)]) == E.DLLM_ERR_INVALID_ARG
+    import torch
+    if not torch.cuda.is_available():
+        # valid arguments reach the device query and report the missing GPU
+        assert step(B=2, L=256, seqs=((4, 0, 256), (16, 0, 256))) == E.DLLM_ERR_HIP
+    mtl.dllm_masked_readout_destroy(h)
+
+
 def test_step_out_struct_matches_header():
     """The ctypes struct lists the header's dllm_step_out fields in order."""
     text = open(HEADER).read()
@@ -148,6 +178,9 @@ def test_step_out_struct_matches_header():
     assert fields == [f[0] for f in _abi.dllm_step_out._fields_]
     body = re.search(r"typedef struct \{([^}]*)\} dllm_policy;", text).group(1)
     assert re.findall(r"(\w+);", body) == [f[0] for f in _abi.dllm_policy._fields_]
+    body = re.search(r"typedef struct \{([^}]*)\} dllm_seq;", text).group(1)
+    assert re.findall(r"(\w+);", body) == [f[0] for f in _abi.dllm_seq._fields_]
+    assert int(re.search(r"#define DLLM_BATCH_MAX (\d+)", text).group(1)) == _abi.DLLM_BATCH_MAX
 
 
 def test_step_without_device_reports_hip_error():
