@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the masked-token readout on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llada|tiny|dream|lc_low|lc_high]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llada|llada_b16|tiny|dream|lc_low|lc_high]
                     [--score conf|margin|neg_entropy] [--tau T]
 
 A step is one denoising readout (compaction, masked LM-head GEMM with the
@@ -11,7 +11,9 @@ V=126464) decoded semi-autoregressively: the last 1024 positions are masked,
 blocks of 32, k=2 per step, 32 consecutive steps with the mask/token state
 carried on the device and the hidden states re-drawn every step; after 32
 steps the state is reset from a pristine device copy (inside the timed
-region).  All inputs are resident in HBM before timing starts.
+region).  All inputs are resident in HBM before timing starts.  The
+llada_b16 workload decodes 16 such sequences together in one batched step
+per denoising step (they share W_lm's single pass).
 
 Prints ONE JSON line: masked tokens/s, the GEMM kernel's roofline (HIP
 events around its launch on the library's stream), and the fp64 CPU
@@ -36,7 +38,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 WORKLOADS = {"tiny": "tiny", "llada": "llada_like_semi_ar", "dream": "dream_like",
-             "lc_low": "long_ctx_low_mask", "lc_high": "long_ctx_high_mask"}
+             "lc_low": "long_ctx_low_mask", "lc_high": "long_ctx_high_mask",
+             "llada_b16": "llada_like_semi_ar_batch16"}
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 CSRC = os.path.join(ROOT, "masked_token_logits_amd", "csrc")
@@ -183,13 +186,21 @@ def main(argv=None) -> int:
     dev = torch.device("cuda", 0)
     t_gen = time.perf_counter()
     W = WL.w_lm(cfg)
-    mask0, tok0 = WL.initial_state(cfg)
-    n_hidden = cfg.steps
-    hidden_steps = [WL.hidden(cfg, W, t)[0] for t in range(n_hidden)]
+    Bq = cfg.batch
+    if Bq > 1:
+        states = [WL.initial_state(cfg, b) for b in range(Bq)]
+        mask0 = np.stack([m for m, _ in states])
+        tok0 = np.stack([t for _, t in states])
+    else:
+        mask0, tok0 = WL.initial_state(cfg)
+    Wt = torch.from_numpy(W.view(np.int16)).to(dev)
+    hidden_steps, Hts = [], []
+    for t in range(cfg.steps):   # upload step by step; batched host copies are dropped
+        h = WL.hidden_batch(cfg, W, t) if Bq > 1 else WL.hidden(cfg, W, t)[0]
+        Hts.append(torch.from_numpy(h.view(np.int16)).to(dev))
+        hidden_steps.append(None if Bq > 1 else h)
     log(f"[bench] generated {args.workload} inputs in {time.perf_counter() - t_gen:.1f}s")
 
-    Wt = torch.from_numpy(W.view(np.int16)).to(dev)
-    Hts = [torch.from_numpy(h.view(np.int16)).to(dev) for h in hidden_steps]
     m_pristine = torch.from_numpy(mask0).to(dev)
     t_pristine = torch.from_numpy(tok0).to(dev)
     mt = m_pristine.clone()
@@ -198,12 +209,13 @@ def main(argv=None) -> int:
     torch.cuda.reset_peak_memory_stats()
 
     stream = torch.cuda.current_stream(dev)
-    rd = mtl.MaskedReadout(Wt, cfg.L, cfg.k, stream=stream)
+    rd = mtl.MaskedReadout(Wt, cfg.L * Bq, cfg.k, stream=stream)
     if args.slices:
         rd.set_slices(args.slices)
     total = args.warmup + args.steps
-    m_slots = torch.zeros(total, dtype=torch.int32, device=dev)
+    m_slots = torch.zeros((total, Bq), dtype=torch.int32, device=dev)
     lo, hi = cfg.win
+    seqs = [(cfg.k, lo, hi)] * Bq
     hip = Hip()
     ev = [(hip.event(), hip.event()) for _ in range(args.steps)]
 
@@ -217,8 +229,11 @@ def main(argv=None) -> int:
         else:
             a, b = ev[timed_index]
             mtl.dllm_masked_readout_set_gemm_events(rd.handle, a, b)
-        out = {"m_out": m_slots.data_ptr() + 4 * i}
-        rd.step(Hts[t], mt, tt, cfg.k, lo, hi, cfg.block, out=out, score=args.score, tau=args.tau)
+        out = {"m_out": m_slots.data_ptr() + 4 * Bq * i}
+        if Bq > 1:
+            rd.step_batch(Hts[t], mt, tt, seqs, cfg.block, out=out, score=args.score, tau=args.tau)
+        else:
+            rd.step(Hts[t], mt, tt, cfg.k, lo, hi, cfg.block, out=out, score=args.score, tau=args.tau)
 
     for i in range(args.warmup):
         one(i, None)
@@ -230,7 +245,7 @@ def main(argv=None) -> int:
     elapsed = time.perf_counter() - t0
     log(f"[bench] timed {args.steps} steps in {elapsed * 1e3:.2f} ms")
 
-    Ms = m_slots.cpu().numpy().astype(np.int64)
+    Ms = m_slots.cpu().numpy().astype(np.int64).sum(axis=1)   # candidate rows per step, all sequences
     timed_M = Ms[args.warmup:]
     masked_rows = int(timed_M.sum())
     gemm_ms = np.array([hip.elapsed_ms(a, b) for a, b in ev])
@@ -241,13 +256,33 @@ def main(argv=None) -> int:
 
     d, V = cfg.d, cfg.V
     ext = args.score != "conf"
-    small = (min(cfg.block, hi - lo) if cfg.block else hi - lo) <= 32
-    if small:
+    small = Bq * (min(cfg.block, hi - lo) if cfg.block else hi - lo) <= 32
+    rec_bytes = 24 if ext else 16
+    slices = (V + 127) // 128
+    if Bq > 1:
+        # Batched steps range from HBM-bound (few rows: W_lm's stream) to
+        # MFMA-bound (many rows).  The bound is the one that takes longer at
+        # the published peaks over the timed steps; both figures are kept.
+        flops = 2.0 * timed_M * d * V
+        bytes_per = V * d * 2 + timed_M * d * 2 + timed_M * 4   # W_lm once, the rows, the row outputs
+        t_mfma = float(flops.sum()) / (BF16_PEAK_TFLOPS * 1e12)
+        t_hbm = float(bytes_per.sum()) / (HBM_PEAK_GBS * 1e9)
+        secs = gemm_ms.sum() * 1e-3
+        if t_mfma >= t_hbm:
+            achieved = float(flops.sum()) / secs / 1e12
+            roof = dict(bound="mfma", achieved=round(achieved, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                        frac=round(achieved / BF16_PEAK_TFLOPS, 4))
+        else:
+            achieved = float(bytes_per.sum()) / secs / 1e9
+            roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                        frac=round(achieved / HBM_PEAK_GBS, 4))
+        roof["mfma_tflops"] = round(float(flops.sum()) / secs / 1e12, 1)
+        roof["hbm_gbs"] = round(float(bytes_per.sum()) / secs / 1e9, 1)
+        roof["roofline_time_frac"] = round(max(t_mfma, t_hbm) / secs, 4)
+    elif small:
         # HBM-bound: every launch streams all of W_lm once plus the gathered
         # rows, and writes one partial record per (row, vocabulary slice):
         # 16 B (max, argmax, sum), 24 B with the margin / entropy terms.
-        slices = (V + 127) // 128
-        rec_bytes = 24 if ext else 16
         bytes_per = V * d * 2 + timed_M * d * 2 + timed_M * slices * rec_bytes + timed_M * 4
         achieved = float(bytes_per.sum()) / (gemm_ms.sum() * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
@@ -259,6 +294,8 @@ def main(argv=None) -> int:
                     frac=round(achieved / BF16_PEAK_TFLOPS, 4))
     src = os.path.join(CSRC, "gemm_online.hip" if small else "gemm_persistent.hip")
     roof["traffic"] = None if ext else traffic_from_profile(args.workload, src)
+    if Bq > 1:
+        roof["kernel"] = "k_gemm_persistent<%s>" % ("true" if ext else "false")
     roof["kernel"] = ("k_gemm_online<SmallTile, %s>" if small else "k_gemm_persistent<%s>") % (
         "true" if ext else "false")
     roof["kernel_avg_us"] = round(float(gemm_ms.mean()) * 1e3, 2)
@@ -279,7 +316,9 @@ def main(argv=None) -> int:
         "data": "synthetic (seeded; random-init LM head of the named shape, no checkpoint or dataset)",
         "config": {
             "workload": f"{cfg.name} (L={cfg.L}, d={d}, V={V}, k={cfg.k}"
-                        + (f", block={cfg.block}, {cfg.steps}-step semi-AR loop" if cfg.block else "") + ")",
+                        + (f", block={cfg.block}, {cfg.steps}-step semi-AR loop" if cfg.block else "")
+                        + (f", {Bq} sequences per batched step" if Bq > 1 else "") + ")",
+            "batch": Bq,
             "L": cfg.L, "d": d, "V": V, "k": cfg.k,
             "masked_rows_timed": masked_rows,
             "peak_mem_bytes": peak_mem,
@@ -292,7 +331,13 @@ def main(argv=None) -> int:
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
-        rec["cpu_baseline"] = cpu_baseline(cfg, W, hidden_steps, mask0, tok0)
+        if Bq > 1:
+            # the oracle steps each sequence on its own: time sequence 0's pass
+            hs0 = [WL.hidden(cfg, W, t, seq=0)[0] for t in range(cfg.steps)]
+            rec["cpu_baseline"] = cpu_baseline(cfg, W, hs0, mask0[0], tok0[0])
+            rec["cpu_baseline"]["sample"] += " (sequence 0 of the batch; sequences are independent)"
+        else:
+            rec["cpu_baseline"] = cpu_baseline(cfg, W, hidden_steps, mask0, tok0)
     else:
         rec["cpu_baseline"] = None
     print(json.dumps(rec), flush=True)

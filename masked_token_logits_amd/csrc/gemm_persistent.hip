@@ -250,103 +250,135 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_persistent(const uint16_t* __res
       else
         fb[f] = *reinterpret_cast<const bf16x8*>(&lds[slot][1][0] + (wr * 128 + f * 32 + frag_row) * BK + chunk);
     };
-    auto load_frags = [&](int slot, int kk, bf16x8* fa, bf16x8* fb) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) load_frag(slot, kk, i, fa, fb);
-    };
 
-    // Prologue: stages 0..2 in flight, wait for stage 0, queue stage 3,
-    // fetch stage 0's first fragments.
-#pragma unroll
-    for (int p = 0; p < NST - 1; ++p) issue_next();
-    stage_sync<2 * DMA_PER_STAGE>();
-    issue_next();
-    bf16x8 fxa[4], fxb[4], fya[4], fyb[4];
-    load_frags(0, 0, fxa, fxb);
+    // The item's tiles for a wave whose NFR (0..4) first 32-row blocks hold
+    // candidate rows (the rest of a partial row tile is padding): MFMAs,
+    // hidden fragment loads and the epilogue run for those blocks only,
+    // while every wave issues the same DMAs and meets the same barriers.
+    auto run_tiles = [&](auto nfr_tag) {
+      constexpr int NFR = decltype(nfr_tag)::value;
+      // Fragment i of a K step: W_lm block i/2 when i is even (needed while
+      // any block is active), hidden block i/2 when odd (if that block is).
+      auto frag = [&](int slot, int kk, int i, bf16x8* fa, bf16x8* fb) {
+        if ((i & 1) == 0 ? NFR > 0 : (i >> 1) < NFR) load_frag(slot, kk, i, fa, fb);
+      };
 
-    // One stage q: load the second K step's fragments while the first K
-    // step's 16 MFMAs run; mid-stage barrier (stage q+1 landed, everyone is
-    // done with stage q); queue stage q+4 into stage q's slot and load stage
-    // q+1's first fragments while the second K step's 16 MFMAs run.  The
-    // sched_group_barrier pattern spreads the fragment loads and DMAs
-    // between the MFMAs, so the matrix pipe never waits on a burst of memory
-    // instructions.  FIRST = first stage of a vocabulary tile: its first
-    // MFMAs take an inline zero accumulator instead of acc, so acc is never
-    // explicitly cleared (explicit clears get hoisted above the epilogue's
-    // reads and force the accumulators out of AGPRs).
-    f32x16 acc[4][4];
-    const f32x16 zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    int q = 0;
-    auto stage = [&](auto first_tag) {
-      constexpr bool FIRST = decltype(first_tag)::value;
-      // First K step: MFMA pair m (blocks 2m, 2m+1), then the second K
-      // step's fragment m.  sched_barrier fixes the interleave.
+      // Prologue: stages 0..2 in flight, wait for stage 0, queue stage 3,
+      // fetch stage 0's first fragments.
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int fv = (2 * m + t) >> 2, fr = (2 * m + t) & 3;
-          acc[fv][fr] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fxa[fv], fxb[fr], FIRST ? zero16 : acc[fv][fr], 0,
-                                                                0, 0);
-        }
-        load_frag(q & (NST - 1), 1, m, fya, fyb);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      for (int p = 0; p < NST - 1; ++p) issue_next();
       stage_sync<2 * DMA_PER_STAGE>();
-      // Second K step: MFMA pair m, DMA m of stage q+4 (into stage q's
-      // slot), fragment m of stage q+1's first K step.
+      issue_next();
+      bf16x8 fxa[4], fxb[4], fya[4], fyb[4];
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int fv = (2 * m + t) >> 2, fr = (2 * m + t) & 3;
-          acc[fv][fr] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fya[fv], fyb[fr], acc[fv][fr], 0, 0, 0);
-        }
-        issue_dma(m);
-        load_frag((q + 1) & (NST - 1), 0, m, fxa, fxb);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      advance_issue();
-      ++q;
-    };
-    for (int vt = vt_lo; vt < vt_hi; ++vt) {
-      stage(std::true_type{});
-      for (int ks = 1; ks < KT; ++ks) stage(std::false_type{});
+      for (int i = 0; i < 8; ++i) frag(0, 0, i, fxa, fxb);
 
-      // Online reduction of the finished vocabulary tile, one 16-value block
-      // at a time.  Accumulator x of block (fv, fr) is vocabulary entry
-      // v0 + fv*32 + 8*(x/4) + x%4 of row wr*128 + fr*32 + lane%32, with
-      // v0 = tile base + wv*128 + 4*(lane/32).  Within a lane the index grows
-      // with (fv, x); strict '>' comparisons in that order keep the lowest
-      // index among equal maxima.
-      // The accumulators are read with explicit v_accvgpr_read (inline asm):
-      // left to itself the register allocator copies all 256 of them to
-      // VGPRs at once and spills.  The compiler does not see these reads as
-      // consumers of the MFMA results for hazard purposes, so 24 wait states
-      // are inserted first, ordered after every MFMA by taking all
-      // accumulators as operands.
-      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::"a"(acc[0][0]), "a"(acc[0][1]), "a"(acc[0][2]),
-                   "a"(acc[0][3]), "a"(acc[1][0]), "a"(acc[1][1]), "a"(acc[1][2]), "a"(acc[1][3]), "a"(acc[2][0]),
-                   "a"(acc[2][1]), "a"(acc[2][2]), "a"(acc[2][3]), "a"(acc[3][0]), "a"(acc[3][1]), "a"(acc[3][2]),
-                   "a"(acc[3][3]));
-      const int v0 = vt * BN + wv * 128 + 4 * frag_half;
-      const bool full = (vt + 1) * BN <= V;
-      auto off = [](int x) { return 8 * (x >> 2) + (x & 3); };
+      // One stage q: load the second K step's fragments while the first K
+      // step's 16 MFMAs run; mid-stage barrier (stage q+1 landed, everyone is
+      // done with stage q); queue stage q+4 into stage q's slot and load stage
+      // q+1's first fragments while the second K step's 16 MFMAs run.  The
+      // sched_barrier pattern spreads the fragment loads and DMAs between the
+      // MFMAs, so the matrix pipe never waits on a burst of memory
+      // instructions.  FIRST = first stage of a vocabulary tile: its first
+      // MFMAs take an inline zero accumulator instead of acc, so acc is never
+      // explicitly cleared (explicit clears get hoisted above the epilogue's
+      // reads and force the accumulators out of AGPRs).
+      f32x16 acc[4][4];
+      const f32x16 zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      int q = 0;
+      auto stage = [&](auto first_tag) {
+        constexpr bool FIRST = decltype(first_tag)::value;
+        // First K step: MFMA pair m (blocks 2m, 2m+1), then the second K
+        // step's fragment m.  sched_barrier fixes the interleave.
 #pragma unroll
-      for (int fr = 0; fr < 4; ++fr) {
+        for (int m = 0; m < 8; ++m) {
 #pragma unroll
-        for (int fv = 0; fv < 4; ++fv) {
-          float z[16];
-#pragma unroll
-          for (int x = 0; x < 16; ++x) {
-            asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(z[x]) : "a"(acc[fv][fr][x]));
-            if (!full && v0 + fv * 32 + off(x) >= V) z[x] = -INFINITY;
+          for (int t = 0; t < 2; ++t) {
+            const int fv = (2 * m + t) >> 2, fr = (2 * m + t) & 3;
+            if (fr < NFR)
+              acc[fv][fr] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fxa[fv], fxb[fr], FIRST ? zero16 : acc[fv][fr],
+                                                                    0, 0, 0);
           }
-          RowState r = get(fr);
-          row_fold<EXT, 16>(r, z, v0 + fv * 32, off);
-          put(fr, r);
+          frag(q & (NST - 1), 1, m, fya, fyb);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        stage_sync<2 * DMA_PER_STAGE>();
+        // Second K step: MFMA pair m, DMA m of stage q+4 (into stage q's
+        // slot), fragment m of stage q+1's first K step.
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const int fv = (2 * m + t) >> 2, fr = (2 * m + t) & 3;
+            if (fr < NFR) acc[fv][fr] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fya[fv], fyb[fr], acc[fv][fr], 0, 0, 0);
+          }
+          issue_dma(m);
+          frag((q + 1) & (NST - 1), 0, m, fxa, fxb);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        advance_issue();
+        ++q;
+      };
+      for (int vt = vt_lo; vt < vt_hi; ++vt) {
+        stage(std::true_type{});
+        for (int ks = 1; ks < KT; ++ks) stage(std::false_type{});
+        if constexpr (NFR > 0) {
+          // Online reduction of the finished vocabulary tile, one 16-value
+          // block at a time.  Accumulator x of block (fv, fr) is vocabulary
+          // entry v0 + fv*32 + 8*(x/4) + x%4 of row wr*128 + fr*32 + lane%32,
+          // with v0 = tile base + wv*128 + 4*(lane/32).  Within a lane the
+          // index grows with (fv, x); strict '>' comparisons in that order
+          // keep the lowest index among equal maxima.
+          // The accumulators are read with explicit v_accvgpr_read (inline
+          // asm): left to itself the register allocator copies all 256 of
+          // them to VGPRs at once and spills.  The compiler does not see these
+          // reads as consumers of the MFMA results for hazard purposes, so 24
+          // wait states are inserted first, ordered after every MFMA by
+          // taking all live accumulators as operands.
+          if constexpr (NFR == 4)
+            asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::"a"(acc[0][0]), "a"(acc[0][1]), "a"(acc[0][2]),
+                         "a"(acc[0][3]), "a"(acc[1][0]), "a"(acc[1][1]), "a"(acc[1][2]), "a"(acc[1][3]),
+                         "a"(acc[2][0]), "a"(acc[2][1]), "a"(acc[2][2]), "a"(acc[2][3]), "a"(acc[3][0]),
+                         "a"(acc[3][1]), "a"(acc[3][2]), "a"(acc[3][3]));
+          else if constexpr (NFR == 3)
+            asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::"a"(acc[0][0]), "a"(acc[0][1]), "a"(acc[0][2]),
+                         "a"(acc[1][0]), "a"(acc[1][1]), "a"(acc[1][2]), "a"(acc[2][0]), "a"(acc[2][1]),
+                         "a"(acc[2][2]), "a"(acc[3][0]), "a"(acc[3][1]), "a"(acc[3][2]));
+          else if constexpr (NFR == 2)
+            asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::"a"(acc[0][0]), "a"(acc[0][1]), "a"(acc[1][0]),
+                         "a"(acc[1][1]), "a"(acc[2][0]), "a"(acc[2][1]), "a"(acc[3][0]), "a"(acc[3][1]));
+          else
+            asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::"a"(acc[0][0]), "a"(acc[1][0]), "a"(acc[2][0]),
+                         "a"(acc[3][0]));
+          const int v0 = vt * BN + wv * 128 + 4 * frag_half;
+          const bool full = (vt + 1) * BN <= V;
+          auto off = [](int x) { return 8 * (x >> 2) + (x & 3); };
+#pragma unroll
+          for (int fr = 0; fr < NFR; ++fr) {
+#pragma unroll
+            for (int fv = 0; fv < 4; ++fv) {
+              float z[16];
+#pragma unroll
+              for (int x = 0; x < 16; ++x) {
+                asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(z[x]) : "a"(acc[fv][fr][x]));
+                if (!full && v0 + fv * 32 + off(x) >= V) z[x] = -INFINITY;
+              }
+              RowState r = get(fr);
+              row_fold<EXT, 16>(r, z, v0 + fv * 32, off);
+              put(fr, r);
+            }
+          }
         }
       }
+    };
+    // 32-row blocks of this wave's 128 rows that hold candidate rows
+    const int nfr = min(4, max(0, (M - row0 - wr * 128 + 31) / 32));
+    switch (nfr) {
+      case 4: run_tiles(std::integral_constant<int, 4>{}); break;
+      case 3: run_tiles(std::integral_constant<int, 3>{}); break;
+      case 2: run_tiles(std::integral_constant<int, 2>{}); break;
+      case 1: run_tiles(std::integral_constant<int, 1>{}); break;
+      default: run_tiles(std::integral_constant<int, 0>{}); break;
     }
 
     // Half-waves hold the same rows with interleaved vocabulary entries.

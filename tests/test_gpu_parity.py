@@ -186,3 +186,18 @@ def test_slice_count_invariance_and_repeats():
         g = run_step(rd, Ht, mt.clone(), tt.clone(), 32, 0, L)
         for key in ("sel_idx", "sel_tok", "sel_conf", "row_tok", "row_conf", "row_lse", "mask", "tokens"):
             np.testing.assert_array_equal(g[key], first[key])
+
+
+@pytest.mark.parametrize("M", [33, 63, 64, 65, 96, 127, 128, 129, 160, 200, 255, 256, 257, 300, 383, 385, 511, 513])
+def test_persistent_partial_row_tiles(M):
+    """Candidate counts around every 32-row block boundary of the 256-row
+    tile: waves whose rows are partly or wholly padding skip those blocks."""
+    rng = np.random.default_rng(100 + M)
+    L, d, V = 600, 128, 1100
+    H = _rand_bf16(rng, (L, d))
+    W = _rand_bf16(rng, (V, d), 0.05)
+    mask = np.zeros(L, np.uint8)
+    mask[rng.choice(L, size=M, replace=False)] = 1
+    tokens = np.full(L, V, np.int32)
+    for slices in (0, 3):
+        _parity_case(H, W, mask, tokens, min(M, 20), slices=slices, where=f"M={M} slices={slices}")
