@@ -18,3 +18,4 @@ from .readout import (  # noqa: F401
     readout_rows,
     StepResult,
 )
+from .ffn import silu, ffn_rows, ffn_chunked  # noqa: F401,E402

@@ -89,3 +89,17 @@ def test_batch_sequences_draw_their_own_bytes():
     inp = WL.make_batch(cfg)
     assert inp.mask.shape == (3, 64) and np.all(inp.mask[:, 32:] == 1) and np.all(inp.mask[:, :32] == 0)
     assert WL.sha256(inp.tokens[1]) != WL.sha256(inp.tokens[0])
+
+
+def test_ffn_inputs():
+    cfg = WL.FFN_WORKLOADS["ffn_tiny"]
+    Wg, Wu, Wd = WL.ffn_weights(cfg)
+    assert Wg.shape == Wu.shape == (cfg.F, cfg.d) and Wd.shape == (cfg.d, cfg.F)
+    assert len({WL.sha256(Wg), WL.sha256(Wu), WL.sha256(Wd)}) == 3
+    X = WL.ffn_input(cfg)
+    assert X.shape == (cfg.L, cfg.d)
+    rms = np.sqrt((WL.bf16_to_f32(X).astype(np.float64) ** 2).mean(axis=1))
+    np.testing.assert_allclose(rms, 1.0, atol=5e-3)
+    np.testing.assert_array_equal(WL.ffn_input(cfg), X)
+    big = WL.FFN_WORKLOADS["ffn_long_ctx_low_mask"]
+    assert (big.L, big.d, big.F) == (131072, 4096, 12288) and big.F % 128 == 0 and big.d % 256 == 0

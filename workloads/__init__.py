@@ -40,6 +40,7 @@ import numpy as np
 
 SEED_ROOT = 0xD11A
 STREAM_W, STREAM_HIDDEN, STREAM_MASK, STREAM_PLANT = 0, 1, 2, 3
+STREAM_FFN_GATE, STREAM_FFN_UP, STREAM_FFN_DOWN = 4, 5, 6
 CHUNK = 1 << 22          # elements per independently seeded chunk
 W_STD = 0.02             # W_lm ~ N(0, 0.02): 0.02 is the standard deviation
 RMS_EPS = 1e-6           # RMS normalisation of the LLaDA-like hidden states
@@ -275,6 +276,39 @@ def make_batch(cfg_or_name, W_bits: np.ndarray | None = None) -> BatchInputs:
     states = [initial_state(cfg, b) for b in range(cfg.batch)]
     return BatchInputs(cfg, W, hidden_batch(cfg, W, 0), np.stack([m for m, _ in states]),
                        np.stack([t for _, t in states]))
+
+
+@dataclass(frozen=True)
+class FFNConfig:
+    """A SwiGLU FFN over all L positions of one step, run ``chunk`` rows at a
+    time (the FFN memory peak at low mask ratio: Mosaic, Abstract and
+    Fig. 3).  Weights N(0, 0.02); inputs are RMS-normalised N(0, 1) rows,
+    drawn like the LLaDA-like hidden states."""
+    id: int
+    name: str
+    L: int
+    d: int
+    F: int
+    chunk: int
+    rms_norm: bool = True
+
+
+FFN_WORKLOADS: dict[str, FFNConfig] = {c.name: c for c in (
+    FFNConfig(7, "ffn_tiny", L=600, d=256, F=384, chunk=256),
+    FFNConfig(8, "ffn_long_ctx_low_mask", L=131072, d=4096, F=12288, chunk=8192),
+)}
+
+
+def ffn_weights(cfg: FFNConfig) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """(W_gate [F, d], W_up [F, d], W_down [d, F]) bf16 bits, N(0, 0.02)."""
+    return (_normal_bf16(cfg.F, cfg.d, W_STD, cfg.id, STREAM_FFN_GATE),
+            _normal_bf16(cfg.F, cfg.d, W_STD, cfg.id, STREAM_FFN_UP),
+            _normal_bf16(cfg.d, cfg.F, W_STD, cfg.id, STREAM_FFN_DOWN))
+
+
+def ffn_input(cfg: FFNConfig) -> np.ndarray:
+    """FFN input rows X [L, d] (bf16 bits)."""
+    return _normal_bf16(cfg.L, cfg.d, 1.0, cfg.id, STREAM_HIDDEN, 0, rms_norm=cfg.rms_norm)
 
 
 def sha256(a: np.ndarray) -> str:
