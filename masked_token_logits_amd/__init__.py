@@ -25,6 +25,9 @@ from ._abi import (  # noqa: F401
     EXPORTED,
     LIB_PATH,
     DllmError,
+    dllm_ffn_pack_gate_up,
+    dllm_ffn_swiglu_chunked,
+    dllm_ffn_workspace_bytes,
     dllm_masked_readout_create,
     dllm_masked_readout_destroy,
     dllm_masked_readout_set_gemm_events,
@@ -39,6 +42,40 @@ from ._abi import (  # noqa: F401
     load,
     make_policy,
 )
+
+
+class SwiGLUFFN:
+    """The sequence-chunked SwiGLU FFN: packed gate/up weights, W_down and
+    a torch-allocated [chunk, F] activation workspace.
+
+    ``W_gate``/``W_up`` [F, d] and ``W_down`` [d, F] are bf16 (or int16 bit
+    pattern) CUDA tensors; W_down must stay alive as long as this object."""
+
+    def __init__(self, W_gate, W_up, W_down, chunk: int, stream=None):
+        import torch
+        F, d = W_gate.shape
+        self.F, self.d, self.chunk = int(F), int(d), int(chunk)
+        self.stream = stream if stream is not None else torch.cuda.current_stream(W_gate.device)
+        self.W_gu = torch.empty((2 * self.F, self.d), dtype=W_gate.dtype, device=W_gate.device)
+        st = dllm_ffn_pack_gate_up(W_gate, W_up, self.F, self.d, self.W_gu, self.stream)
+        if st != DLLM_OK:
+            raise DllmError(st, "dllm_ffn_pack_gate_up")
+        self.W_down = W_down
+        nbytes = dllm_ffn_workspace_bytes(self.chunk, self.F)
+        if nbytes == 0:
+            raise DllmError(DLLM_ERR_INVALID_ARG, "dllm_ffn_workspace_bytes")
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=W_gate.device)
+
+    def __call__(self, X, Y=None):
+        """Queue Y = FFN(X) (X [L, d]); returns Y (new unless given; may be X)."""
+        import torch
+        if Y is None:
+            Y = torch.empty_like(X)
+        st = dllm_ffn_swiglu_chunked(X, int(X.shape[0]), self.d, self.W_gu, self.W_down, self.F, self.chunk, Y,
+                                     self.workspace, int(self.workspace.numel()), self.stream)
+        if st != DLLM_OK:
+            raise DllmError(st, "dllm_ffn_swiglu_chunked")
+        return Y
 
 
 class MaskedReadout:

@@ -36,6 +36,9 @@ EXPORTED = (
     "dllm_status_string",
     "dllm_masked_readout_set_slices",
     "dllm_masked_readout_set_gemm_events",
+    "dllm_ffn_workspace_bytes",
+    "dllm_ffn_pack_gate_up",
+    "dllm_ffn_swiglu_chunked",
 )
 
 
@@ -107,6 +110,13 @@ def load(path: str = LIB_PATH):
     lib.dllm_masked_readout_set_slices.argtypes = [C.c_void_p, C.c_int32]
     lib.dllm_masked_readout_set_gemm_events.restype = C.c_int
     lib.dllm_masked_readout_set_gemm_events.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p]
+    lib.dllm_ffn_workspace_bytes.restype = C.c_size_t
+    lib.dllm_ffn_workspace_bytes.argtypes = [C.c_int64, C.c_int64]
+    lib.dllm_ffn_pack_gate_up.restype = C.c_int
+    lib.dllm_ffn_pack_gate_up.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_void_p]
+    lib.dllm_ffn_swiglu_chunked.restype = C.c_int
+    lib.dllm_ffn_swiglu_chunked.argtypes = [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_void_p, C.c_int64,
+                                            C.c_int64, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
     _lib = lib
     return lib
 
@@ -195,6 +205,20 @@ def dllm_masked_readout_step_batch(handle, B: int, hidden, L: int, mask, tokens,
                                                  seqs, int(block),
                                                  C.byref(policy) if policy is not None else None,
                                                  C.byref(so) if so is not None else None)
+
+
+def dllm_ffn_workspace_bytes(chunk: int, F: int) -> int:
+    return int(load().dllm_ffn_workspace_bytes(chunk, F))
+
+
+def dllm_ffn_pack_gate_up(W_gate, W_up, F: int, d: int, W_gu, stream=None) -> int:
+    return load().dllm_ffn_pack_gate_up(_ptr(W_gate), _ptr(W_up), F, d, _ptr(W_gu), _stream(stream))
+
+
+def dllm_ffn_swiglu_chunked(X, L: int, d: int, W_gu, W_down, F: int, chunk: int, Y, workspace,
+                            workspace_bytes: int, stream=None) -> int:
+    return load().dllm_ffn_swiglu_chunked(_ptr(X), L, d, _ptr(W_gu), _ptr(W_down), F, chunk, _ptr(Y),
+                                          _ptr(workspace), workspace_bytes, _stream(stream))
 
 
 def dllm_masked_readout_destroy(handle) -> int:

@@ -13,7 +13,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libdllm_readout.so")
-SOURCES = ["readout.hip", "mask_compact.hip", "gemm_online.hip", "gemm_persistent.hip", "merge_select.hip"]
+SOURCES = ["readout.hip", "mask_compact.hip", "gemm_online.hip", "gemm_persistent.hip", "merge_select.hip",
+           "ffn.hip"]
 ARCH = "gfx950"
 
 

@@ -26,6 +26,10 @@
 //     always lands at LDS base + 16 * lane.
 //   * The gather is fused: the hidden rows of a row tile are resolved once
 //     through idx[] per work item.
+//   * The same main loop serves the FFN's GEMMs (MODE = kEpiStore /
+//     kEpiSwiGLU): rows are then contiguous, every item is exactly one
+//     256 x 256 output tile, and the epilogue stores bf16 (for the gate/up
+//     projection, SiLU(gate) * up of paired 32-row weight blocks).
 //   * Work items are (row tile, vocabulary slice) pairs of the device-side
 //     plan (ctr[3] = slices, ctr[4] = row tiles) written by the compaction
 //     kernel once M is known.  Workgroup b takes items q(b), q(b) + G, ...,
@@ -111,18 +115,35 @@ __device__ __forceinline__ void stage_sync() {
   asm volatile("" ::: "memory");
 }
 
-template <bool EXT>
+// Round-to-nearest-even float -> bfloat16 bits (finite inputs), two per word.
+__device__ __forceinline__ uint32_t bf16_pack2(float lo, float hi) {
+  uint32_t a = __float_as_uint(lo), b = __float_as_uint(hi);
+  a += 0x7FFFu + ((a >> 16) & 1u);
+  b += 0x7FFFu + ((b >> 16) & 1u);
+  return (a >> 16) | (b & 0xFFFF0000u);
+}
+
+// SiLU(g) * u in fp32: g / (1 + 2^(-g log2 e)) * u.
+__device__ __forceinline__ float swiglu(float g, float u) {
+  return g / (1.0f + __builtin_amdgcn_exp2f(-g * kLog2eF)) * u;
+}
+
+// MODE: kEpiReadout = online vocabulary reduction into per-slice partials
+// (rows gathered through idx, M / slices / row tiles from ctr); kEpiStore /
+// kEpiSwiGLU = bf16 output tiles (rows row 0..M-1 of H, shape from st).
+template <int MODE, bool EXT>
 __global__ __launch_bounds__(NT, 1) void k_gemm_persistent(const uint16_t* __restrict__ W,
                                                           const uint16_t* __restrict__ H, int d, int V,
                                                           const int32_t* __restrict__ idx,
-                                                          const int32_t* __restrict__ ctr, Partials part) {
+                                                          const int32_t* __restrict__ ctr, Partials part,
+                                                          StoreArgs st) {
   __shared__ __attribute__((aligned(1024))) uint16_t lds[NST][2][TILE];
 
-  const int M = ctr[0];
-  const int S = ctr[3];
-  const int n_rt = ctr[4];
-  const int n_items = n_rt * S;
   const int n_vt = (V + BN - 1) / BN;
+  const int M = MODE == kEpiReadout ? ctr[0] : st.M;
+  const int S = MODE == kEpiReadout ? ctr[3] : n_vt;           // store modes: one output tile per item
+  const int n_rt = MODE == kEpiReadout ? ctr[4] : (st.M + BM - 1) / BM;
+  const int n_items = n_rt * S;
   const int KT = d / BK;
 
   const int tid = threadIdx.x;
@@ -162,7 +183,8 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_persistent(const uint16_t* __res
     for (int i = 0; i < DMA_PER_OPERAND; ++i) {
       int r = row0 + (wave + 4 * i) * DMA_ROWS + dma_row;
       r = r < M ? r : M - 1;
-      hoff[i] = ((uint32_t)idx[r] * (uint32_t)d + (uint32_t)(dma_chunk * 8)) * 2u;
+      const uint32_t src = MODE == kEpiReadout ? (uint32_t)idx[r] : (uint32_t)r;
+      hoff[i] = (src * (uint32_t)d + (uint32_t)(dma_chunk * 8)) * 2u;
     }
     uint32_t woff[DMA_PER_OPERAND];
 #pragma unroll
@@ -350,22 +372,74 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_persistent(const uint16_t* __res
           else
             asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::"a"(acc[0][0]), "a"(acc[1][0]), "a"(acc[2][0]),
                          "a"(acc[3][0]));
-          const int v0 = vt * BN + wv * 128 + 4 * frag_half;
-          const bool full = (vt + 1) * BN <= V;
-          auto off = [](int x) { return 8 * (x >> 2) + (x & 3); };
+          if constexpr (MODE == kEpiReadout) {
+            const int v0 = vt * BN + wv * 128 + 4 * frag_half;
+            const bool full = (vt + 1) * BN <= V;
+            auto off = [](int x) { return 8 * (x >> 2) + (x & 3); };
 #pragma unroll
-          for (int fr = 0; fr < NFR; ++fr) {
+            for (int fr = 0; fr < NFR; ++fr) {
 #pragma unroll
-            for (int fv = 0; fv < 4; ++fv) {
-              float z[16];
+              for (int fv = 0; fv < 4; ++fv) {
+                float z[16];
 #pragma unroll
-              for (int x = 0; x < 16; ++x) {
-                asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(z[x]) : "a"(acc[fv][fr][x]));
-                if (!full && v0 + fv * 32 + off(x) >= V) z[x] = -INFINITY;
+                for (int x = 0; x < 16; ++x) {
+                  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(z[x]) : "a"(acc[fv][fr][x]));
+                  if (!full && v0 + fv * 32 + off(x) >= V) z[x] = -INFINITY;
+                }
+                RowState r = get(fr);
+                row_fold<EXT, 16>(r, z, v0 + fv * 32, off);
+                put(fr, r);
               }
-              RowState r = get(fr);
-              row_fold<EXT, 16>(r, z, v0 + fv * 32, off);
-              put(fr, r);
+            }
+          } else {
+            // Output tile store (the item's only tile: these stores come after
+            // the last stage's waits, and the item's vmcnt(0) drains them).
+            // Accumulator x of block (fv, fr) is output column
+            // c0 + fv*32 + 8*(x/4) + x%4, c0 = tile base + wv*128 + 4*(lane/32),
+            // of row wr*128 + fr*32 + lane%32: four runs of 4 columns.
+#pragma unroll
+            for (int fr = 0; fr < NFR; ++fr) {
+              const int row = row0 + wr * 128 + fr * 32 + frag_row;
+              const bool ok = row < M;
+              uint16_t* orow = st.out + (size_t)(ok ? row : 0) * (size_t)st.ldo;
+              if constexpr (MODE == kEpiStore) {
+                const int c0 = vt * BN + wv * 128 + 4 * frag_half;
+#pragma unroll
+                for (int fv = 0; fv < 4; ++fv) {
+#pragma unroll
+                  for (int j = 0; j < 4; ++j) {
+                    float z[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                      asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(z[i]) : "a"(acc[fv][fr][4 * j + i]));
+                    const uint2 pk = make_uint2(bf16_pack2(z[0], z[1]), bf16_pack2(z[2], z[3]));
+                    if (ok) *reinterpret_cast<uint2*>(orow + c0 + fv * 32 + 8 * j) = pk;
+                  }
+                }
+              } else {
+                // Weight rows come in 64-row units: 32 gate rows, then the 32
+                // up rows of the same outputs.  Blocks (0, 1) and (2, 3) of a
+                // wave are such pairs, so gate and up of one output sit in the
+                // same lane and register position.  Output column
+                // c0 + p*32 + 8*(x/4) + x%4, c0 = tile*128 + wv*64 + 4*(lane/32).
+                const int c0 = vt * (BN / 2) + wv * 64 + 4 * frag_half;
+#pragma unroll
+                for (int pr = 0; pr < 2; ++pr) {
+#pragma unroll
+                  for (int j = 0; j < 4; ++j) {
+                    float a[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                      float g, u;
+                      asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(g) : "a"(acc[2 * pr][fr][4 * j + i]));
+                      asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(u) : "a"(acc[2 * pr + 1][fr][4 * j + i]));
+                      a[i] = swiglu(g, u);
+                    }
+                    const uint2 pk = make_uint2(bf16_pack2(a[0], a[1]), bf16_pack2(a[2], a[3]));
+                    if (ok) *reinterpret_cast<uint2*>(orow + c0 + pr * 32 + 8 * j) = pk;
+                  }
+                }
+              }
             }
           }
         }
@@ -381,63 +455,65 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_persistent(const uint16_t* __res
       default: run_tiles(std::integral_constant<int, 0>{}); break;
     }
 
-    // Half-waves hold the same rows with interleaved vocabulary entries.
-#pragma unroll
-    for (int fr = 0; fr < 4; ++fr) {
-      RowState x = get(fr), y;
-      y.m = __shfl_xor(x.m, 32);
-      y.s = __shfl_xor(x.s, 32);
-      y.m2 = __shfl_xor(x.m2, 32);
-      y.t = __shfl_xor(x.t, 32);
-      y.a = __shfl_xor(x.a, 32);
-      row_merge<EXT>(x, y);
-      put(fr, x);
-    }
-    // The two vocabulary halves (wv = 0, 1) of each row meet in LDS.  All DMAs
-    // have landed (the last stage waited for vmcnt(0)); barrier before reuse.
-    stage_sync<0>();
-    float* xm = reinterpret_cast<float*>(&lds[0][0][0]);
-    int* xa = reinterpret_cast<int*>(xm + 2 * BM);
-    float* xs = reinterpret_cast<float*>(xa + 2 * BM);
-    float* xm2 = xs + 2 * BM;
-    float* xt = xm2 + 2 * BM;
-    if (frag_half == 0) {
-#pragma unroll
+    if constexpr (MODE == kEpiReadout) {
+      // Half-waves hold the same rows with interleaved vocabulary entries.
+  #pragma unroll
       for (int fr = 0; fr < 4; ++fr) {
-        const int r = wr * 128 + fr * 32 + frag_row;
-        xm[wv * BM + r] = run_m[fr];
-        xa[wv * BM + r] = run_a[fr];
-        xs[wv * BM + r] = run_s[fr];
-        if (EXT) {
-          xm2[wv * BM + r] = run_m2[fr];
-          xt[wv * BM + r] = run_t[fr];
+        RowState x = get(fr), y;
+        y.m = __shfl_xor(x.m, 32);
+        y.s = __shfl_xor(x.s, 32);
+        y.m2 = __shfl_xor(x.m2, 32);
+        y.t = __shfl_xor(x.t, 32);
+        y.a = __shfl_xor(x.a, 32);
+        row_merge<EXT>(x, y);
+        put(fr, x);
+      }
+      // The two vocabulary halves (wv = 0, 1) of each row meet in LDS.  All DMAs
+      // have landed (the last stage waited for vmcnt(0)); barrier before reuse.
+      stage_sync<0>();
+      float* xm = reinterpret_cast<float*>(&lds[0][0][0]);
+      int* xa = reinterpret_cast<int*>(xm + 2 * BM);
+      float* xs = reinterpret_cast<float*>(xa + 2 * BM);
+      float* xm2 = xs + 2 * BM;
+      float* xt = xm2 + 2 * BM;
+      if (frag_half == 0) {
+  #pragma unroll
+        for (int fr = 0; fr < 4; ++fr) {
+          const int r = wr * 128 + fr * 32 + frag_row;
+          xm[wv * BM + r] = run_m[fr];
+          xa[wv * BM + r] = run_a[fr];
+          xs[wv * BM + r] = run_s[fr];
+          if (EXT) {
+            xm2[wv * BM + r] = run_m2[fr];
+            xt[wv * BM + r] = run_t[fr];
+          }
         }
       }
-    }
-    stage_sync<0>();
-    {
-      const int r = tid;  // NT == BM: one row per thread
-      RowState x, y;
-      x.m = xm[r];
-      x.a = xa[r];
-      x.s = xs[r];
-      x.m2 = EXT ? xm2[r] : -INFINITY;
-      x.t = EXT ? xt[r] : 0.f;
-      y.m = xm[BM + r];
-      y.a = xa[BM + r];
-      y.s = xs[BM + r];
-      y.m2 = EXT ? xm2[BM + r] : -INFINITY;
-      y.t = EXT ? xt[BM + r] : 0.f;
-      row_merge<EXT>(x, y);
-      const int row = row0 + r;
-      if (row < M) {
-        const size_t o = (size_t)row * (size_t)S + (size_t)slice;
-        part.m[o] = x.m;
-        part.a[o] = x.a;
-        part.s[o] = x.s;
-        if (EXT) {
-          part.m2[o] = x.m2;
-          part.t[o] = x.t;
+      stage_sync<0>();
+      {
+        const int r = tid;  // NT == BM: one row per thread
+        RowState x, y;
+        x.m = xm[r];
+        x.a = xa[r];
+        x.s = xs[r];
+        x.m2 = EXT ? xm2[r] : -INFINITY;
+        x.t = EXT ? xt[r] : 0.f;
+        y.m = xm[BM + r];
+        y.a = xa[BM + r];
+        y.s = xs[BM + r];
+        y.m2 = EXT ? xm2[BM + r] : -INFINITY;
+        y.t = EXT ? xt[BM + r] : 0.f;
+        row_merge<EXT>(x, y);
+        const int row = row0 + r;
+        if (row < M) {
+          const size_t o = (size_t)row * (size_t)S + (size_t)slice;
+          part.m[o] = x.m;
+          part.a[o] = x.a;
+          part.s[o] = x.s;
+          if (EXT) {
+            part.m2[o] = x.m2;
+            part.t[o] = x.t;
+          }
         }
       }
     }
@@ -453,10 +529,26 @@ static_assert(NT == BM, "one thread per row in the final merge");
 
 hipError_t launch_gemm_persistent(const uint16_t* W, const uint16_t* H, int d, int V, const int32_t* idx,
                                   const int32_t* ctr, int grid, Partials p, hipStream_t stream) {
+  const StoreArgs none = {nullptr, 0, 0};
   if (p.ext)
-    hipLaunchKernelGGL(k_gemm_persistent<true>, dim3(grid), dim3(NT), 0, stream, W, H, d, V, idx, ctr, p);
+    hipLaunchKernelGGL((k_gemm_persistent<kEpiReadout, true>), dim3(grid), dim3(NT), 0, stream, W, H, d, V, idx, ctr, p,
+                       none);
   else
-    hipLaunchKernelGGL(k_gemm_persistent<false>, dim3(grid), dim3(NT), 0, stream, W, H, d, V, idx, ctr, p);
+    hipLaunchKernelGGL((k_gemm_persistent<kEpiReadout, false>), dim3(grid), dim3(NT), 0, stream, W, H, d, V, idx, ctr,
+                       p, none);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_store(bool swiglu, const uint16_t* W, int n_w_rows, const uint16_t* X, int K, int M,
+                             uint16_t* out, int ldo, int grid, hipStream_t stream) {
+  const Partials none = {};
+  const StoreArgs st = {out, ldo, M};
+  if (swiglu)
+    hipLaunchKernelGGL((k_gemm_persistent<kEpiSwiGLU, false>), dim3(grid), dim3(NT), 0, stream, W, X, K, n_w_rows,
+                       nullptr, nullptr, none, st);
+  else
+    hipLaunchKernelGGL((k_gemm_persistent<kEpiStore, false>), dim3(grid), dim3(NT), 0, stream, W, X, K, n_w_rows,
+                       nullptr, nullptr, none, st);
   return hipGetLastError();
 }
 

@@ -100,6 +100,19 @@ constexpr int kPersistBM = 256, kPersistBN = 256, kPersistBK = 32, kPersistStage
 hipError_t launch_gemm_persistent(const uint16_t* W, const uint16_t* H, int d, int V, const int32_t* idx,
                                   const int32_t* ctr, int grid, Partials p, hipStream_t stream);
 
+// The persistent GEMM's store epilogues (FFN): out[M, ldo] (bf16) = X[M, K] . W^T,
+// W [n_w_rows, K]; n_w_rows % 256 == 0.  swiglu: W holds gate/up rows in
+// 64-row units (32 gate rows, then the 32 up rows of the same outputs) and
+// out gets SiLU(gate) * up, n_w_rows / 2 columns.
+constexpr int kEpiReadout = 0, kEpiStore = 1, kEpiSwiGLU = 2;
+struct StoreArgs {
+  uint16_t* out;
+  int ldo;
+  int M;
+};
+hipError_t launch_gemm_store(bool swiglu, const uint16_t* W, int n_w_rows, const uint16_t* X, int K, int M,
+                             uint16_t* out, int ldo, int grid, hipStream_t stream);
+
 hipError_t launch_gemm_small(const uint16_t* W, const uint16_t* H, int d, int V, const int32_t* idx,
                              const int32_t* ctr, int slices, Partials p, hipStream_t stream);
 

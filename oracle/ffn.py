@@ -33,14 +33,15 @@ def ffn_rows(X_bits: np.ndarray, Wg_bits: np.ndarray, Wu_bits: np.ndarray, Wd_bi
     """SwiGLU FFN of the given rows in fp64.
 
     X [n, d], W_gate / W_up [F, d], W_down [d, F] (bf16 bits).  Returns
-    (Y [n, d], A [n, F]) and, with ``want_bound``, also |A| . |W_down|^T, the
-    sum of absolute terms of every output (for rounding-error bounds)."""
+    (Y [n, d], A [n, F]) and, with ``want_bound``, also the sums over f of
+    |A_f W_down[j, f]| and of (A_f W_down[j, f])^2 for every output (the
+    scales of rounding errors in its terms)."""
     X = widen_bf16(X_bits)
     Wg, Wu, Wd = widen_bf16(Wg_bits), widen_bf16(Wu_bits), widen_bf16(Wd_bits)
     A = silu(X @ Wg.T) * (X @ Wu.T)
     Y = A @ Wd.T
     if want_bound:
-        return Y, A, np.abs(A) @ np.abs(Wd).T
+        return Y, A, np.abs(A) @ np.abs(Wd).T, (A * A) @ (Wd * Wd).T
     return Y, A
 
 

@@ -11,6 +11,8 @@ from masked_token_logits_amd import _abi
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "dllm_readout.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 # Fake but 256-byte aligned device addresses: validation never dereferences them.
 FAKE = 0x7F0000000000
@@ -22,8 +24,11 @@ def lib():
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    return sorted(set(re.findall(r"\b(dllm_\w+)\s*\(", text)))
+    """Every dllm_* function declared in include/*.h."""
+    names = set()
+    for h in HEADERS:
+        names |= set(re.findall(r"\b(dllm_\w+)\s*\(", open(h).read()))
+    return sorted(names)
 
 
 def test_header_declares_the_three_calls():
@@ -195,3 +200,31 @@ def test_step_without_device_reports_hip_error():
 
 def test_destroy_null():
     assert mtl.dllm_masked_readout_destroy(None) == mtl.DLLM_OK
+
+
+def test_ffn_validation_before_any_hip_call():
+    E = mtl
+    assert mtl.dllm_ffn_workspace_bytes(8192, 12288) == 8192 * 12288 * 2
+    assert mtl.dllm_ffn_workspace_bytes(0, 128) == 0 and mtl.dllm_ffn_workspace_bytes(8, 0) == 0
+    X, Wgu, Wd, Y, ws = FAKE, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000, FAKE + 0x400000
+
+    def ffn(X=X, L=1000, d=256, Wgu=Wgu, Wd=Wd, F=384, chunk=256, Y=Y, ws=ws, nbytes=1 << 30):
+        return mtl.dllm_ffn_swiglu_chunked(X, L, d, Wgu, Wd, F, chunk, Y, ws, nbytes)
+
+    assert ffn(X=None) == E.DLLM_ERR_INVALID_ARG
+    assert ffn(Y=None) == E.DLLM_ERR_INVALID_ARG
+    assert ffn(L=-1) == E.DLLM_ERR_INVALID_ARG
+    assert ffn(chunk=0) == E.DLLM_ERR_INVALID_ARG
+    assert ffn(d=200) == E.DLLM_ERR_UNSUPPORTED            # d % 256
+    assert ffn(F=200) == E.DLLM_ERR_UNSUPPORTED            # F % 128
+    assert ffn(chunk=1 << 20, F=4096, d=4096) == E.DLLM_ERR_UNSUPPORTED   # 32-bit row offsets
+    assert ffn(X=X + 8) == E.DLLM_ERR_UNSUPPORTED
+    assert ffn(ws=None) == E.DLLM_ERR_WORKSPACE
+    assert ffn(nbytes=100) == E.DLLM_ERR_WORKSPACE
+    assert ffn(L=0) == E.DLLM_OK                           # nothing to queue
+    assert mtl.dllm_ffn_pack_gate_up(None, FAKE, 128, 64, FAKE) == E.DLLM_ERR_INVALID_ARG
+    assert mtl.dllm_ffn_pack_gate_up(FAKE, FAKE, 100, 64, FAKE) == E.DLLM_ERR_UNSUPPORTED
+    assert mtl.dllm_ffn_pack_gate_up(FAKE, FAKE, 128, 12, FAKE) == E.DLLM_ERR_UNSUPPORTED
+    import torch
+    if not torch.cuda.is_available():
+        assert ffn() == E.DLLM_ERR_HIP

@@ -85,6 +85,12 @@ def test_ffn_chunk_invariance_and_row_independence():
 def test_ffn_bound_dominates_terms():
     rng = np.random.default_rng(73)
     X, Wg, Wu, Wd = _bf(rng, (4, 32)), _bf(rng, (20, 32), 0.2), _bf(rng, (20, 32), 0.2), _bf(rng, (32, 20), 0.2)
-    Y, A, B = oracle.ffn_rows(X, Wg, Wu, Wd, want_bound=True)
+    Y, A, B, Q = oracle.ffn_rows(X, Wg, Wu, Wd, want_bound=True)
     assert np.all(B >= np.abs(Y) - 1e-12)
-    np.testing.assert_allclose(B, np.abs(A) @ np.abs(oracle.widen_bf16(Wd)).T)
+    wd = oracle.widen_bf16(Wd)
+    for i in range(4):
+        for j in (0, 7, 31):
+            terms = [A[i, f] * wd[j, f] for f in range(20)]
+            assert abs(B[i, j] - math.fsum(abs(t) for t in terms)) < 1e-12
+            assert abs(Q[i, j] - math.fsum(t * t for t in terms)) < 1e-12
+    assert np.all(np.sqrt(Q) <= B + 1e-12)
