@@ -1,7 +1,8 @@
 #!/usr/bin/env python3
 """Benchmark of the masked-token readout on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llada|llada_b16|tiny|dream|lc_low|lc_high]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+                    [--workload llada|llada_b16|tiny|dream|lc_low|lc_high|ffn|ffn_tiny]
                     [--score conf|margin|neg_entropy] [--tau T]
 
 A step is one denoising readout (compaction, masked LM-head GEMM with the
@@ -20,7 +21,9 @@ events around its launch on the library's stream), and the fp64 CPU
 oracle timed on a bounded sample of the same workload.  ``--score`` and
 ``--tau`` time another selection policy (ranking by top-2 margin or negative
 entropy, whose statistics the GEMM then also accumulates; threshold commits
-with cap k) instead of the default top-k by confidence.
+with cap k) instead of the default top-k by confidence.  ``--workload ffn``
+times the sequence-chunked SwiGLU FFN of one layer over the 128k-context
+LLaDA-like sequence (chunks of 8192 rows) instead of the readout.
 """
 from __future__ import annotations
 
@@ -40,6 +43,7 @@ if ROOT not in sys.path:
 WORKLOADS = {"tiny": "tiny", "llada": "llada_like_semi_ar", "dream": "dream_like",
              "lc_low": "long_ctx_low_mask", "lc_high": "long_ctx_high_mask",
              "llada_b16": "llada_like_semi_ar_batch16"}
+FFN_WORKLOADS = {"ffn": "ffn_long_ctx_low_mask", "ffn_tiny": "ffn_tiny"}
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 CSRC = os.path.join(ROOT, "masked_token_logits_amd", "csrc")
@@ -141,12 +145,101 @@ def cpu_baseline(cfg, W, hidden_steps, mask0, tok0, n_rows_sample: int = 512):
                 sample=sample, seconds=round(dt, 3))
 
 
+def cpu_baseline_ffn(cfg, X, Wg, Wu, Wd, budget_s: float = 10.0):
+    """The fp64 FFN oracle as it stands, on consecutive blocks of rows until
+    about ``budget_s`` seconds have passed."""
+    import oracle
+    t0 = time.perf_counter()
+    rows = 0
+    while rows < cfg.L and (rows == 0 or time.perf_counter() - t0 < budget_s):
+        n = min(512, cfg.L - rows)
+        oracle.ffn_rows(X[rows:rows + n], Wg, Wu, Wd)
+        rows += n
+    dt = time.perf_counter() - t0
+    return dict(value=rows / dt, unit="tokens/s", cores=blas_threads(), kind="oracle",
+                sample=f"first {rows} rows of the sequence, blocks of 512 (fp64 gate/up/down GEMMs)",
+                seconds=round(dt, 3))
+
+
+def bench_ffn(args, name: str) -> int:
+    """One FFN layer over the whole sequence per step."""
+    import numpy as np
+    import torch
+
+    import masked_token_logits_amd as mtl
+    import workloads as WL
+
+    cfg = WL.FFN_WORKLOADS[name]
+    t_gen = time.perf_counter()
+    Wg, Wu, Wd = WL.ffn_weights(cfg)
+    X = WL.ffn_input(cfg)
+    log(f"[bench] generated {name} inputs in {time.perf_counter() - t_gen:.1f}s")
+    dev = torch.device("cuda", 0)
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+    Xt, Wgt, Wut, Wdt = to(X), to(Wg), to(Wu), to(Wd)
+    Yt = torch.empty_like(Xt)
+    ffn = mtl.SwiGLUFFN(Wgt, Wut, Wdt, cfg.chunk)
+    del Wgt, Wut
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    base_mem = int(torch.cuda.memory_allocated())
+    for _ in range(args.warmup):
+        ffn(Xt, Yt)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record()
+        ffn(Xt, Yt)
+        b.record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    step_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    peak = int(torch.cuda.max_memory_allocated())
+    flops = 6.0 * cfg.L * cfg.d * cfg.F
+    achieved = flops / (float(step_ms.mean()) * 1e-3) / 1e12
+    rec = {
+        "metric": "FFN tokens/sec (sequence-chunked SwiGLU FFN, one layer)",
+        "value": round(cfg.L * args.steps / elapsed, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; random-init FFN weights of the named shape, no checkpoint or dataset)",
+        "config": {
+            "workload": f"{cfg.name} (L={cfg.L}, d={cfg.d}, F={cfg.F}, chunk={cfg.chunk}; one layer per step)",
+            "L": cfg.L, "d": cfg.d, "F": cfg.F, "chunk": cfg.chunk,
+            "transient_bytes": int(ffn.workspace.numel()),
+            "unchunked_gate_up_act_bf16_bytes": 3 * cfg.L * cfg.F * 2,
+            "peak_mem_bytes": peak,
+            "resident_before_step_bytes": base_mem,
+            "parallelism": "single GPU",
+        },
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "k_gemm_persistent<kEpiSwiGLU> + k_gemm_persistent<kEpiStore> (both GEMMs of a step)",
+                     "kernel_avg_us": round(float(step_ms.mean()) * 1e3, 2)},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        rec["cpu_baseline"] = cpu_baseline_ffn(cfg, X, Wg, Wu, Wd)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=320)
     ap.add_argument("--warmup", type=int, default=32)
-    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="llada")
+    ap.add_argument("--workload", choices=sorted(WORKLOADS) + sorted(FFN_WORKLOADS), default="llada")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     ap.add_argument("--slices", type=int, default=0, help="force the GEMM's vocabulary slice count")
     ap.add_argument("--score", choices=["conf", "margin", "neg_entropy"], default="conf",
@@ -182,6 +275,8 @@ def main(argv=None) -> int:
         print(json.dumps({"copy_calibration_bytes": 1 << 30, "copies": 3}))
         return 0
     mtl.load()
+    if args.workload in FFN_WORKLOADS:
+        return bench_ffn(args, FFN_WORKLOADS[args.workload])
     cfg = WL.WORKLOADS[WORKLOADS[args.workload]]
     dev = torch.device("cuda", 0)
     t_gen = time.perf_counter()
