@@ -22,6 +22,7 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kPerThread = 16;
 constexpr int kChunk = kThreads * kPerThread;
+static_assert(kPerThread == 16, "mask_bits16 covers 16 positions");
 
 // Work plan once M is known (every thread of the workgroup calls this):
 // fixed slices, or for the persistent GEMM the slice count S minimising
@@ -48,6 +49,25 @@ __device__ void choose_plan(int M, const PlanParams& plan, unsigned long long* s
   S = (*s_best == ~0ull) ? 1 : (int)(*s_best & 0xFFFFF);
 }
 
+// Bits j = 0..15 set where position p0 + j < hi holds a mask flag
+// (p0 >= the window start).  One 16-byte load when the 16 bytes are aligned
+// and inside the window, else byte loads.
+__device__ __forceinline__ unsigned mask_bits16(const uint8_t* __restrict__ m, int p0, int hi) {
+  unsigned bits = 0;
+  if (p0 + 16 <= hi && (((uintptr_t)(m + p0)) & 15u) == 0) {
+    const uint4 v = *reinterpret_cast<const uint4*>(m + p0);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int by = 0; by < 4; ++by) bits |= ((w[q] >> (8 * by)) & 0xFFu) ? (1u << (4 * q + by)) : 0u;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) bits |= (p0 + j < hi && m[p0 + j] != 0) ? (1u << j) : 0u;
+  }
+  return bits;
+}
+
 // ---- one-wave building blocks of the batched compaction -------------------
 // Lanes cover 16 consecutive mask bytes each, 1024 positions per pass.
 
@@ -57,13 +77,9 @@ __device__ void wave_block_window(const uint8_t* __restrict__ m, int64_t block, 
   const int lane = threadIdx.x & 63;
   int first = hi;
   for (int base = lo; base < hi; base += 64 * 16) {
-    int mine = hi;
     const int p0 = base + lane * 16;
-#pragma unroll
-    for (int j = 15; j >= 0; --j) {
-      const int p = p0 + j;
-      if (p < hi && m[p] != 0) mine = p;
-    }
+    const unsigned bits = p0 < hi ? mask_bits16(m, p0, hi) : 0u;
+    const int mine = bits ? p0 + __ffs(bits) - 1 : hi;
     const unsigned long long bal = __ballot(mine < hi);  // lanes cover increasing positions
     if (bal) {
       first = __shfl(mine, __ffsll((long long)bal) - 1);
@@ -86,11 +102,7 @@ __device__ int wave_count(const uint8_t* __restrict__ m, int lo, int hi) {
   int c = 0;
   for (int base = lo; base < hi; base += 64 * 16) {
     const int p0 = base + lane * 16;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int p = p0 + j;
-      c += (p < hi && m[p] != 0) ? 1 : 0;
-    }
+    c += p0 < hi ? __popc(mask_bits16(m, p0, hi)) : 0;
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off);
@@ -105,12 +117,7 @@ __device__ void wave_write(const uint8_t* __restrict__ m, int lo, int hi, int32_
   int running = 0;
   for (int base = lo; base < hi; base += 64 * 16) {
     const int p0 = base + lane * 16;
-    unsigned bits = 0;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int p = p0 + j;
-      if (p < hi && m[p] != 0) bits |= 1u << j;
-    }
+    unsigned bits = p0 < hi ? mask_bits16(m, p0, hi) : 0u;
     const int c = __popc(bits);
     int pre = 0;
 #pragma unroll
@@ -144,14 +151,9 @@ __global__ __launch_bounds__(kThreads) void k_mask_compact(const uint8_t* __rest
     if (tid == 0) s_first = hi;
     __syncthreads();
     for (int base = lo; base < hi; base += kChunk) {
-      int mine = hi;
       const int p0 = base + tid * kPerThread;
-#pragma unroll
-      for (int j = kPerThread - 1; j >= 0; --j) {
-        const int p = p0 + j;
-        if (p < hi && mask[p] != 0) mine = p;
-      }
-      if (mine < hi) atomicMin(&s_first, mine);
+      const unsigned fb = p0 < hi ? mask_bits16(mask, p0, hi) : 0u;
+      if (fb) atomicMin(&s_first, p0 + __ffs(fb) - 1);
       __syncthreads();
       const bool found = s_first < hi;
       __syncthreads();
@@ -173,12 +175,7 @@ __global__ __launch_bounds__(kThreads) void k_mask_compact(const uint8_t* __rest
   int running = 0;
   for (int base = lo; base < hi; base += kChunk) {
     const int p0 = base + tid * kPerThread;
-    unsigned bits = 0;
-#pragma unroll
-    for (int j = 0; j < kPerThread; ++j) {
-      const int p = p0 + j;
-      if (p < hi && mask[p] != 0) bits |= 1u << j;
-    }
+    unsigned bits = p0 < hi ? mask_bits16(mask, p0, hi) : 0u;
     const int c = __popc(bits);
     int pre = 0;
 #pragma unroll
@@ -285,13 +282,9 @@ __global__ __launch_bounds__(64) void k_mask_compact_small(const uint8_t* __rest
   if (block > 0) {
     int first = hi;
     for (int base = lo; base < hi; base += 64 * 16) {
-      int mine = hi;
       const int p0 = base + lane * 16;
-#pragma unroll
-      for (int j = 15; j >= 0; --j) {
-        const int p = p0 + j;
-        if (p < hi && mask[p] != 0) mine = p;
-      }
+      const unsigned fb = p0 < hi ? mask_bits16(mask, p0, hi) : 0u;
+      const int mine = fb ? p0 + __ffs(fb) - 1 : hi;
       // lowest position over the wave: lanes cover increasing positions
       const unsigned long long bal = __ballot(mine < hi);
       if (bal) {

@@ -148,6 +148,31 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_scatter(
     if (o.m_out) o.m_out[b] = M;
   }
   if (n <= 0) return;
+  const size_t sbase = (size_t)b * (size_t)k_stride;
+
+  if (M <= kSelThreads) {
+    // Few rows: every thread ranks its key by counting the larger keys (keys
+    // are unique), in LDS; no radix passes.
+    uint64_t* kl = sel;   // kTopkCap >= kSelThreads
+    if (tid < M) kl[tid] = kb[tid];
+    __syncthreads();
+    if (tid < M) {
+      const uint64_t key = kl[tid];
+      int rank = 0;
+      for (int i = 0; i < M; ++i) rank += kl[i] > key ? 1 : 0;
+      if (rank < n) {
+        const int row = start + tid;
+        const int pos = idx[row];
+        const int tok = row_tok[row];
+        tokens[pos] = tok;
+        mask[pos] = 0;
+        if (o.sel_idx) o.sel_idx[sbase + rank] = (int32_t)(pos - pos_base);
+        if (o.sel_tok) o.sel_tok[sbase + rank] = tok;
+        if (o.sel_conf) o.sel_conf[sbase + rank] = row_conf[row];
+      }
+    }
+    return;
+  }
 
   uint64_t prefix = 0, pmask = 0;
   if (n < M) {
@@ -217,7 +242,6 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_scatter(
       __syncthreads();
     }
   }
-  const size_t sbase = (size_t)b * (size_t)k_stride;
   for (int i = tid; i < n; i += kSelThreads) {
     const uint64_t key = sel[i];
     const int row = (int)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFu));
@@ -243,6 +267,7 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_scatter(
 constexpr int kFinishThreads = 1024;
 static_assert(kFinishThreads == 32 * kSmallBM, "32 lanes per row");
 static_assert(kBatchMax <= kFinishThreads, "one thread per sequence");
+static_assert(kTopkCap >= kSelThreads, "few-row ranking keeps the keys in sel[]");
 template <bool EXT>
 __global__ __launch_bounds__(kFinishThreads) void k_finish_small(const int32_t* __restrict__ ctr,
                                                                 const int32_t* __restrict__ idx,
