@@ -64,6 +64,8 @@ def test_tiny_config_parity():
     (2, 1100, 136, 2999, 0.3, 100),      # odd V, several slices
     (3, 513, 512, 700, 1.0, 64),         # fully masked, ragged last row tile
     (4, 257, 8, 33, 0.5, 3),             # d = 8, V < one tile
+    (5, 400, 160, 1500, 0.8, 25),        # d = 5 x 32: an odd number of 32-deep K stages
+    (6, 600, 320, 1300, 0.7, 30),        # d = 10 x 32
 ])
 def test_ragged_shapes_large_path(seed, L, d, V, frac, k):
     rng = np.random.default_rng(seed)
