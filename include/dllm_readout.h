@@ -53,7 +53,7 @@ typedef struct dllm_readout dllm_readout; /* opaque host-side handle */
 typedef enum {
   DLLM_OK = 0,
   DLLM_ERR_INVALID_ARG = 1, /* null pointer, size or range out of bounds */
-  DLLM_ERR_UNSUPPORTED = 2, /* d % 8 != 0, a pointer not 16-byte aligned, k_max too large */
+  DLLM_ERR_UNSUPPORTED = 2, /* shape not divisible as required, pointer misaligned, size over a limit */
   DLLM_ERR_WORKSPACE = 3,   /* workspace null or smaller than dllm_masked_readout_workspace_bytes */
   DLLM_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed (also: no GPU) */
 } dllm_status;

@@ -67,7 +67,8 @@ dllm_status dllm_ffn_swiglu_chunked(const uint16_t* X, int64_t L, int64_t d, con
   if (L < 0 || L >= ((int64_t)1 << 31) || d < 1 || F < 1 || chunk < 1) return DLLM_ERR_INVALID_ARG;
   if (d % 256 != 0 || F % 128 != 0) return DLLM_ERR_UNSUPPORTED;
   const int64_t wide = d > F ? d : F;
-  if (chunk * wide * 2 >= ((int64_t)1 << 32) || 2 * F * d * 2 >= ((int64_t)1 << 40)) return DLLM_ERR_UNSUPPORTED;
+  // the persistent GEMM uses 32-bit byte offsets for the rows of a chunk and of a 256-row weight tile
+  if (chunk * wide * 2 >= ((int64_t)1 << 32) || 256 * wide * 2 >= ((int64_t)1 << 32)) return DLLM_ERR_UNSUPPORTED;
   if (!dllm::aligned16(X) || !dllm::aligned16(W_gu) || !dllm::aligned16(W_down) || !dllm::aligned16(Y))
     return DLLM_ERR_UNSUPPORTED;
   const size_t need = dllm_ffn_workspace_bytes(chunk, F);

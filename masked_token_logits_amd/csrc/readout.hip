@@ -1,5 +1,6 @@
-// Host side of the C ABI: argument checks, workspace carving, choice of the
-// GEMM variant and launch of the four kernels on the handle's stream.
+// Host side of the readout C ABI: argument checks, workspace carving, choice
+// of the GEMM variant and launch of the step's kernels (compaction, GEMM,
+// merge / selection) on the handle's stream.
 #include "../../include/dllm_readout.h"
 #include "readout_internal.h"
 
@@ -136,11 +137,12 @@ dllm_status run_step(dllm_readout* h, const StepArgs& a, const dllm::Policy& pol
 
   // Choose the GEMM variant from the host-known bound on M; the slice count
   // of the persistent variant is fixed on the device once M is known.  The
-  // persistent kernel addresses hidden rows with 32-bit byte offsets, so it
-  // needs the hidden tensor to span less than 4 GiB.
+  // persistent kernel addresses hidden rows and the rows of a W_lm tile with
+  // 32-bit byte offsets, so both must span less than 4 GiB.
   enum { kSmall, kPersistent, kStreaming } path;
   const int64_t n_vt_large = (h->V + dllm::kLargeBN - 1) / dllm::kLargeBN;
-  const bool offsets32 = a.hidden_rows * h->d * 2 < ((int64_t)1 << 32);
+  const bool offsets32 = a.hidden_rows * h->d * 2 < ((int64_t)1 << 32) &&
+                         (int64_t)dllm::kPersistBN * h->d * 2 < ((int64_t)1 << 32);
   dllm::PlanParams plan = {};
   int n_rt = 0;
   if (rows_max <= dllm::kSmallBM) {
@@ -226,7 +228,7 @@ const char* dllm_status_string(dllm_status s) {
   switch (s) {
     case DLLM_OK: return "ok";
     case DLLM_ERR_INVALID_ARG: return "invalid argument";
-    case DLLM_ERR_UNSUPPORTED: return "unsupported argument (d % 8, pointer alignment or k_max)";
+    case DLLM_ERR_UNSUPPORTED: return "unsupported argument (shape divisibility, pointer alignment or size limit)";
     case DLLM_ERR_WORKSPACE: return "workspace missing or too small";
     case DLLM_ERR_HIP: return "HIP runtime error";
   }
