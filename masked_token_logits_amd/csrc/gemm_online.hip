@@ -115,36 +115,43 @@ __global__ __launch_bounds__(T::NT) void k_gemm_online(const uint16_t* __restric
     b_ptr[i] = H + (size_t)idx[r] * (size_t)d;
   }
 
-  bf16x8 ra[T::A_LD], rb[T::B_LD];
   const bf16x8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
 
-  auto gload = [&](int vt, int ks) {
+  // Global -> registers (one register set per stage in flight), registers ->
+  // LDS.  The loads are unconditional: a chunk past d reads the row's last
+  // chunk instead (d % 8 == 0, so that is in bounds) and is replaced by zeros
+  // when stored, so no load sits in a branch and the compiler can leave a
+  // later stage's loads in flight while an earlier stage is stored.
+  auto gload = [&](int vt, int ks, bf16x8* ra, bf16x8* rb) {
     const int k0 = ks * kBK;
     const int v0 = vt * T::BN;
 #pragma unroll
     for (int i = 0; i < T::A_LD; ++i) {
       int v = v0 + a_row[i];
       v = v < V ? v : V - 1;
-      const int k = k0 + a_ch[i] * 8;
+      int k = k0 + a_ch[i] * 8;
+      k = k < d ? k : d - 8;
       const bf16x8* src = reinterpret_cast<const bf16x8*>(W + (size_t)v * (size_t)d + k);
       if constexpr (T::STREAM_W)
-        ra[i] = (k < d) ? __builtin_nontemporal_load(src) : zero8;
+        ra[i] = __builtin_nontemporal_load(src);
       else
-        ra[i] = (k < d) ? *src : zero8;
+        ra[i] = *src;
     }
 #pragma unroll
     for (int i = 0; i < T::B_LD; ++i) {
-      const int k = k0 + b_ch[i] * 8;
-      rb[i] = (k < d) ? *reinterpret_cast<const bf16x8*>(b_ptr[i] + k) : zero8;
+      int k = k0 + b_ch[i] * 8;
+      k = k < d ? k : d - 8;
+      rb[i] = *reinterpret_cast<const bf16x8*>(b_ptr[i] + k);
     }
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](int buf, int ks, const bf16x8* ra, const bf16x8* rb) {
+    const int k0 = ks * kBK;
 #pragma unroll
     for (int i = 0; i < T::A_LD; ++i)
-      *reinterpret_cast<bf16x8*>(&sA[buf][swz(a_row[i], a_ch[i])]) = ra[i];
+      *reinterpret_cast<bf16x8*>(&sA[buf][swz(a_row[i], a_ch[i])]) = k0 + a_ch[i] * 8 < d ? ra[i] : zero8;
 #pragma unroll
     for (int i = 0; i < T::B_LD; ++i)
-      *reinterpret_cast<bf16x8*>(&sB[buf][swz(b_row[i], b_ch[i])]) = rb[i];
+      *reinterpret_cast<bf16x8*>(&sB[buf][swz(b_row[i], b_ch[i])]) = k0 + b_ch[i] * 8 < d ? rb[i] : zero8;
   };
 
   f32x16 acc[T::FV][T::FR];
@@ -159,24 +166,12 @@ __global__ __launch_bounds__(T::NT) void k_gemm_online(const uint16_t* __restric
       for (int e = 0; e < 16; ++e) acc[fv][fr][e] = 0.f;
 
   const int total = (vt_hi - vt_lo) * KT;
-  int vt = vt_lo, ks = 0;
-  gload(vt, ks);
-  lstore(0);
-  __syncthreads();
-
   const int frag_row = lane & 31;
   const int frag_half = lane >> 5;
 
-  for (int s = 0; s < total; ++s) {
-    const int buf = s & 1;
-    int nvt = vt, nks = ks + 1;
-    if (nks == KT) {
-      nks = 0;
-      ++nvt;
-    }
-    const bool has_next = (s + 1) < total;
-    if (has_next) gload(nvt, nks);
-
+  // One stage: the MFMAs on LDS buffer `buf` (stage (vt, ks)), and after the
+  // tile's last K stage the online reduction of the tile.
+  auto body = [&](int buf, int vt, int ks) {
 #pragma unroll
     for (int kk = 0; kk < kBK / 16; ++kk) {
       const int ch = kk * 2 + frag_half;
@@ -224,11 +219,77 @@ __global__ __launch_bounds__(T::NT) void k_gemm_online(const uint16_t* __restric
 #pragma unroll
           for (int e = 0; e < 16; ++e) acc[fv][fr][e] = 0.f;
     }
+  };
+  auto next = [&](int& vt, int& ks) {
+    if (++ks == KT) {
+      ks = 0;
+      ++vt;
+    }
+  };
 
-    if (has_next) lstore(buf ^ 1);
+  if constexpr (T::STREAM_W) {
+    // Few rows, W_lm streamed from HBM: two stages of global loads in flight
+    // (register sets 0 and 1, by stage parity; the loop runs stages in pairs
+    // so the sets are never indexed at run time).  Stage s loads stage s + 2,
+    // computes stage s and stores stage s + 1 (loaded two stages earlier).
+    // Every load and LDS store is unconditional, so no memory operation sits
+    // in a branch and the loads in flight are the same on every path: past
+    // the last stage the loads repeat the last stage (an L2 hit) and the
+    // stores fill a buffer that is never read again.
+    bf16x8 ra0[T::A_LD], rb0[T::B_LD], ra1[T::A_LD], rb1[T::B_LD];
+    int vt = vt_lo, ks = 0;        // stage being computed
+    int ld_vt = vt_lo, ld_ks = 0;  // stage being loaded
+    auto ld_next = [&]() {
+      if (ld_vt != vt_hi - 1 || ld_ks != KT - 1) next(ld_vt, ld_ks);
+    };
+    gload(ld_vt, ld_ks, ra0, rb0);
+    ld_next();
+    gload(ld_vt, ld_ks, ra1, rb1);
+    ld_next();
+    lstore(0, 0, ra0, rb0);
     __syncthreads();
-    vt = nvt;
-    ks = nks;
+    int s = 0;
+    for (; s + 1 < total; s += 2) {
+      gload(ld_vt, ld_ks, ra0, rb0);  // stage s + 2
+      ld_next();
+      int st_vt = vt, st_ks = ks;     // stage s + 1
+      next(st_vt, st_ks);
+      body(0, vt, ks);
+      lstore(1, st_ks, ra1, rb1);
+      __syncthreads();
+      vt = st_vt;
+      ks = st_ks;
+      gload(ld_vt, ld_ks, ra1, rb1);  // stage s + 3
+      ld_next();
+      next(st_vt, st_ks);             // stage s + 2
+      body(1, vt, ks);
+      lstore(0, st_ks, ra0, rb0);
+      __syncthreads();
+      vt = st_vt;
+      ks = st_ks;
+    }
+    if (s < total) {  // odd stage count: the last stage is in buffer 0
+      body(0, vt, ks);
+      __syncthreads();
+    }
+  } else {
+    // One stage of global loads in flight (registers), double-buffered LDS.
+    bf16x8 ra[T::A_LD], rb[T::B_LD];
+    int vt = vt_lo, ks = 0;
+    gload(vt, ks, ra, rb);
+    lstore(0, ks, ra, rb);
+    __syncthreads();
+    for (int s = 0; s < total; ++s) {
+      int nvt = vt, nks = ks;
+      next(nvt, nks);
+      const bool has_next = (s + 1) < total;
+      if (has_next) gload(nvt, nks, ra, rb);
+      body(s & 1, vt, ks);
+      if (has_next) lstore((s & 1) ^ 1, nks, ra, rb);
+      __syncthreads();
+      vt = nvt;
+      ks = nks;
+    }
   }
 
   // Combine the two half-waves (same rows, interleaved vocabulary entries).
