@@ -19,20 +19,25 @@
 //     orientation each lane's 16 accumulators of a 32x32 block are 16
 //     vocabulary entries of ONE row, so most of the reduction is in-lane.
 //   * W_lm and hidden tiles are staged through LDS (BK = 64 bf16 per stage,
-//     double buffered, global loads for stage s+1 in flight while stage s
-//     computes).  16-byte chunks are XOR-swizzled by row so that the
-//     ds_read_b128 fragment loads are bank-conflict free.
+//     double buffered).  The few-row tile, which streams W_lm, keeps two
+//     stages of global loads in flight in registers; the many-row tile one.
+//     16-byte chunks are XOR-swizzled by row so that the ds_read_b128
+//     fragment loads are bank-conflict free.
 //   * The gather is fused: each thread resolves its hidden-row pointers
 //     once through idx[] and streams them; no [M, d] copy exists.
 //   * Workgroup ids are remapped so that the workgroups resident on one XCD
 //     (ids congruent mod 8) own neighbouring (row tile, slice) pairs and
 //     share hidden tiles in that XCD's L2.
 //   * M is read on the device; row tiles past M exit at once, so the host
-//     never waits for the compaction result.
+//     never waits for the compaction result.  For a single sequence the
+//     few-row tile does the compaction itself: its candidate window holds at
+//     most 32 positions, which one wave lists while the first W_lm loads are
+//     in flight, so that step needs no compaction launch.
 #include "readout_internal.h"
 
 #include <math.h>
 
+#include "few_rows.h"
 #include "online_state.h"
 
 namespace dllm {
@@ -51,6 +56,9 @@ __device__ __forceinline__ int xcd_remap(int bid, int grid) {
 template <int BM_, int BN_, int WM_, int WN_, bool STREAM_W_ = false>
 struct Tile {
   static constexpr bool STREAM_W = STREAM_W_;  // W_lm read exactly once: non-temporal loads
+  // waves per SIMD to reserve registers for: the streaming tile's 40 KiB of
+  // LDS allow 4 workgroups (16 waves) per CU, so at most 128 VGPRs
+  static constexpr int MIN_WAVES = STREAM_W ? 4 : 1;
   static constexpr int BM = BM_;             // candidate rows per workgroup
   static constexpr int BN = BN_;             // vocabulary entries per tile
   static constexpr int WM = WM_, WN = WN_;   // waves along rows / vocabulary
@@ -69,24 +77,27 @@ struct Tile {
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * kBK + ((chunk ^ (row & 7)) << 3); }
 
-template <class T, bool EXT>
-__global__ __launch_bounds__(T::NT) void k_gemm_online(const uint16_t* __restrict__ W,
+template <class T, bool EXT, bool FIND>
+__global__ __launch_bounds__(T::NT, T::MIN_WAVES) void k_gemm_online(const uint16_t* __restrict__ W,
                                                        const uint16_t* __restrict__ H, int d, int V,
                                                        const int32_t* __restrict__ idx,
                                                        const int32_t* __restrict__ ctr, int slices,
-                                                       int n_vt, Partials part) {
+                                                       int n_vt, Partials part, FindRows fr) {
+  static_assert(!FIND || (T::STREAM_W && T::BM == kSmallBM), "the row search is the few-row tile's");
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][T::BN * kBK];
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][T::BM * kBK];
 
-  const int M = ctr[0];
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int rt = bid / slices;
   const int slice = bid - rt * slices;
   const int row0 = rt * T::BM;
-  if (row0 >= M) return;
   const int vt_lo = (int)(((int64_t)slice * n_vt) / slices);
   const int vt_hi = (int)(((int64_t)(slice + 1) * n_vt) / slices);
-  if (vt_lo >= vt_hi) return;
+  int M = 0;
+  if constexpr (!FIND) {
+    M = ctr[0];
+    if (row0 >= M || vt_lo >= vt_hi) return;
+  }
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -110,10 +121,16 @@ __global__ __launch_bounds__(T::NT) void k_gemm_online(const uint16_t* __restric
     const int c = i * T::NT + tid;
     b_row[i] = c / T::CPR;
     b_ch[i] = c % T::CPR;
-    int r = row0 + b_row[i];
-    r = r < M ? r : M - 1;  // rows past M read a valid row; their results are dropped
-    b_ptr[i] = H + (size_t)idx[r] * (size_t)d;
   }
+  // Hidden-row pointers through the candidate list (M > 0).
+  auto set_rows = [&](const int32_t* list) {
+#pragma unroll
+    for (int i = 0; i < T::B_LD; ++i) {
+      int r = row0 + b_row[i];
+      r = r < M ? r : M - 1;  // rows past M read a valid row; their results are dropped
+      b_ptr[i] = H + (size_t)list[r] * (size_t)d;
+    }
+  };
 
   const bf16x8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
 
@@ -122,7 +139,7 @@ __global__ __launch_bounds__(T::NT) void k_gemm_online(const uint16_t* __restric
   // chunk instead (d % 8 == 0, so that is in bounds) and is replaced by zeros
   // when stored, so no load sits in a branch and the compiler can leave a
   // later stage's loads in flight while an earlier stage is stored.
-  auto gload = [&](int vt, int ks, bf16x8* ra, bf16x8* rb) {
+  auto gload_w = [&](int vt, int ks, bf16x8* ra) {
     const int k0 = ks * kBK;
     const int v0 = vt * T::BN;
 #pragma unroll
@@ -137,6 +154,9 @@ __global__ __launch_bounds__(T::NT) void k_gemm_online(const uint16_t* __restric
       else
         ra[i] = *src;
     }
+  };
+  auto gload_h = [&](int ks, bf16x8* rb) {
+    const int k0 = ks * kBK;
 #pragma unroll
     for (int i = 0; i < T::B_LD; ++i) {
       int k = k0 + b_ch[i] * 8;
@@ -242,15 +262,51 @@ __global__ __launch_bounds__(T::NT) void k_gemm_online(const uint16_t* __restric
     auto ld_next = [&]() {
       if (ld_vt != vt_hi - 1 || ld_ks != KT - 1) next(ld_vt, ld_ks);
     };
-    gload(ld_vt, ld_ks, ra0, rb0);
+    // The first two stages' W_lm loads go out before the rows are known.
+    gload_w(ld_vt, ld_ks, ra0);
+    const int ks0 = ld_ks;
     ld_next();
-    gload(ld_vt, ld_ks, ra1, rb1);
+    gload_w(ld_vt, ld_ks, ra1);
+    const int ks1 = ld_ks;
     ld_next();
-    lstore(0, 0, ra0, rb0);
+    if constexpr (FIND) {
+      // The step's candidate rows, found by wave 0 while those loads are in
+      // flight (every workgroup finds the same list; workgroup 0 publishes it
+      // for the finish kernel).  Staged in LDS buffer sB[1], not used before
+      // the loop's first store, which follows two barriers.
+      int* s_idx = reinterpret_cast<int*>(&sB[1][0]);
+      if (wave == 0) {
+        const FewRows f = find_few_rows(fr.mask, fr.win_lo, fr.win_hi, fr.block);
+        if (f.cand) {
+          s_idx[f.slot] = f.lo + lane;
+          if (blockIdx.x == 0) fr.idx[f.slot] = f.lo + lane;
+        }
+        if (lane == 0) {
+          s_idx[kSmallBM] = f.M;
+          if (blockIdx.x == 0) {
+            fr.ctr[0] = f.M;
+            fr.ctr[1] = f.lo;
+            fr.ctr[2] = f.hi;
+            fr.ctr[3] = slices;
+            fr.ctr[4] = 1;
+          }
+        }
+      }
+      __syncthreads();
+      M = s_idx[kSmallBM];
+      if (row0 >= M || vt_lo >= vt_hi) return;
+      set_rows(s_idx);
+    } else {
+      set_rows(idx);
+    }
+    gload_h(ks0, rb0);
+    gload_h(ks1, rb1);
+    lstore(0, ks0, ra0, rb0);
     __syncthreads();
     int s = 0;
     for (; s + 1 < total; s += 2) {
-      gload(ld_vt, ld_ks, ra0, rb0);  // stage s + 2
+      gload_w(ld_vt, ld_ks, ra0);  // stage s + 2
+      gload_h(ld_ks, rb0);
       ld_next();
       int st_vt = vt, st_ks = ks;     // stage s + 1
       next(st_vt, st_ks);
@@ -259,7 +315,8 @@ __global__ __launch_bounds__(T::NT) void k_gemm_online(const uint16_t* __restric
       __syncthreads();
       vt = st_vt;
       ks = st_ks;
-      gload(ld_vt, ld_ks, ra1, rb1);  // stage s + 3
+      gload_w(ld_vt, ld_ks, ra1);  // stage s + 3
+      gload_h(ld_ks, rb1);
       ld_next();
       next(st_vt, st_ks);             // stage s + 2
       body(1, vt, ks);
@@ -274,16 +331,21 @@ __global__ __launch_bounds__(T::NT) void k_gemm_online(const uint16_t* __restric
     }
   } else {
     // One stage of global loads in flight (registers), double-buffered LDS.
+    set_rows(idx);
     bf16x8 ra[T::A_LD], rb[T::B_LD];
     int vt = vt_lo, ks = 0;
-    gload(vt, ks, ra, rb);
+    gload_w(vt, ks, ra);
+    gload_h(ks, rb);
     lstore(0, ks, ra, rb);
     __syncthreads();
     for (int s = 0; s < total; ++s) {
       int nvt = vt, nks = ks;
       next(nvt, nks);
       const bool has_next = (s + 1) < total;
-      if (has_next) gload(nvt, nks, ra, rb);
+      if (has_next) {
+        gload_w(nvt, nks, ra);
+        gload_h(nks, rb);
+      }
       body(s & 1, vt, ks);
       if (has_next) lstore((s & 1) ^ 1, nks, ra, rb);
       __syncthreads();
@@ -294,15 +356,7 @@ __global__ __launch_bounds__(T::NT) void k_gemm_online(const uint16_t* __restric
 
   // Combine the two half-waves (same rows, interleaved vocabulary entries).
 #pragma unroll
-  for (int fr = 0; fr < T::FR; ++fr) {
-    RowState y;
-    y.m = __shfl_xor(run[fr].m, 32);
-    y.s = __shfl_xor(run[fr].s, 32);
-    y.m2 = __shfl_xor(run[fr].m2, 32);
-    y.t = __shfl_xor(run[fr].t, 32);
-    y.a = __shfl_xor(run[fr].a, 32);
-    row_merge<EXT>(run[fr], y);
-  }
+  for (int fr = 0; fr < T::FR; ++fr) row_merge<EXT>(run[fr], shfl_xor_state(run[fr], 32));
 
   // Combine the WN waves that share rows, in wave order, through LDS.
   float* xm = reinterpret_cast<float*>(&sA[0][0]);
@@ -310,7 +364,7 @@ __global__ __launch_bounds__(T::NT) void k_gemm_online(const uint16_t* __restric
   float* xs = reinterpret_cast<float*>(xa + T::WN * T::BM);
   float* xm2 = xs + T::WN * T::BM;
   float* xt = xm2 + T::WN * T::BM;
-  static_assert(5 * T::WN * T::BM * 4 <= (int)sizeof(sA), "LDS exchange area too small");
+  static_assert(5 * T::WN * T::BM * 4 <= (int)sizeof(sA[0]), "LDS exchange area too small");
   if (frag_half == 0) {
 #pragma unroll
     for (int fr = 0; fr < T::FR; ++fr) {
@@ -347,8 +401,8 @@ __global__ __launch_bounds__(T::NT) void k_gemm_online(const uint16_t* __restric
       const size_t o = (size_t)row * (size_t)slices + (size_t)slice;
       if constexpr (T::STREAM_W) {
         // few rows: one 16-byte record (m, a, s, 0) per partial in part.m
-        // (and (m2, t) in part.m2), so the single-workgroup finish issues
-        // one load per partial and array
+        // (and (m2, t) in part.m2), so a merge issues one load per
+        // partial and array
         float4 rec;
         rec.x = x.m;
         rec.y = __int_as_float(x.a);
@@ -374,6 +428,7 @@ using LargeTile = Tile<kLargeBM, kLargeBN, 2, 4>;
 // streamed with non-temporal loads (no L2 / Infinity Cache allocation):
 // measured 180 -> 162 us per step on the LLaDA-like head.
 using SmallTile = Tile<kSmallBM, kSmallBN, 1, 4, true>;
+static_assert(kSmallBM + 1 <= SmallTile::BM * kBK / 2, "candidate list must fit in sB[1]");
 
 }  // namespace
 
@@ -381,24 +436,35 @@ hipError_t launch_gemm_large(const uint16_t* W, const uint16_t* H, int d, int V,
                              const int32_t* ctr, int n_row_tiles, int slices, Partials p, hipStream_t stream) {
   const int n_vt = (V + LargeTile::BN - 1) / LargeTile::BN;
   const int grid = n_row_tiles * slices;
+  const FindRows none = {};
   if (p.ext)
-    hipLaunchKernelGGL((k_gemm_online<LargeTile, true>), dim3(grid), dim3(LargeTile::NT), 0, stream, W, H, d, V,
-                       idx, ctr, slices, n_vt, p);
+    hipLaunchKernelGGL((k_gemm_online<LargeTile, true, false>), dim3(grid), dim3(LargeTile::NT), 0, stream, W, H, d,
+                       V, idx, ctr, slices, n_vt, p, none);
   else
-    hipLaunchKernelGGL((k_gemm_online<LargeTile, false>), dim3(grid), dim3(LargeTile::NT), 0, stream, W, H, d, V,
-                       idx, ctr, slices, n_vt, p);
+    hipLaunchKernelGGL((k_gemm_online<LargeTile, false, false>), dim3(grid), dim3(LargeTile::NT), 0, stream, W, H,
+                       d, V, idx, ctr, slices, n_vt, p, none);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_small(const uint16_t* W, const uint16_t* H, int d, int V, const int32_t* idx,
-                             const int32_t* ctr, int slices, Partials p, hipStream_t stream) {
+                             const int32_t* ctr, int slices, Partials p, const FindRows* find, hipStream_t stream) {
   const int n_vt = (V + SmallTile::BN - 1) / SmallTile::BN;
-  if (p.ext)
-    hipLaunchKernelGGL((k_gemm_online<SmallTile, true>), dim3(slices), dim3(SmallTile::NT), 0, stream, W, H, d, V,
-                       idx, ctr, slices, n_vt, p);
-  else
-    hipLaunchKernelGGL((k_gemm_online<SmallTile, false>), dim3(slices), dim3(SmallTile::NT), 0, stream, W, H, d, V,
-                       idx, ctr, slices, n_vt, p);
+  const FindRows fr = find ? *find : FindRows{};
+  if (find) {
+    if (p.ext)
+      hipLaunchKernelGGL((k_gemm_online<SmallTile, true, true>), dim3(slices), dim3(SmallTile::NT), 0, stream, W, H,
+                         d, V, idx, ctr, slices, n_vt, p, fr);
+    else
+      hipLaunchKernelGGL((k_gemm_online<SmallTile, false, true>), dim3(slices), dim3(SmallTile::NT), 0, stream, W,
+                         H, d, V, idx, ctr, slices, n_vt, p, fr);
+  } else {
+    if (p.ext)
+      hipLaunchKernelGGL((k_gemm_online<SmallTile, true, false>), dim3(slices), dim3(SmallTile::NT), 0, stream, W,
+                         H, d, V, idx, ctr, slices, n_vt, p, fr);
+    else
+      hipLaunchKernelGGL((k_gemm_online<SmallTile, false, false>), dim3(slices), dim3(SmallTile::NT), 0, stream, W,
+                         H, d, V, idx, ctr, slices, n_vt, p, fr);
+  }
   return hipGetLastError();
 }
 

@@ -14,6 +14,7 @@
 // The same kernel then fixes how the GEMM splits the work, now that M is
 // known (choose_plan).  A batched step compacts every sequence's window
 // into one list of rows (k_mask_compact_batch).
+#include "few_rows.h"
 #include "readout_internal.h"
 
 namespace dllm {
@@ -47,25 +48,6 @@ __device__ void choose_plan(int M, const PlanParams& plan, unsigned long long* s
   }
   __syncthreads();
   S = (*s_best == ~0ull) ? 1 : (int)(*s_best & 0xFFFFF);
-}
-
-// Bits j = 0..15 set where position p0 + j < hi holds a mask flag
-// (p0 >= the window start).  One 16-byte load when the 16 bytes are aligned
-// and inside the window, else byte loads.
-__device__ __forceinline__ unsigned mask_bits16(const uint8_t* __restrict__ m, int p0, int hi) {
-  unsigned bits = 0;
-  if (p0 + 16 <= hi && (((uintptr_t)(m + p0)) & 15u) == 0) {
-    const uint4 v = *reinterpret_cast<const uint4*>(m + p0);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int by = 0; by < 4; ++by) bits |= ((w[q] >> (8 * by)) & 0xFFu) ? (1u << (4 * q + by)) : 0u;
-  } else {
-#pragma unroll
-    for (int j = 0; j < 16; ++j) bits |= (p0 + j < hi && m[p0 + j] != 0) ? (1u << j) : 0u;
-  }
-  return bits;
 }
 
 // ---- one-wave building blocks of the batched compaction -------------------
@@ -271,43 +253,18 @@ __global__ __launch_bounds__(kThreads) void k_mask_compact_batch(const uint8_t* 
   }
 }
 
-// Small candidate windows (the host knows at most 32 rows can come out): one
-// wave, no barriers.  Block search reads 16 bytes per lane per iteration;
-// the candidate block (<= 32 positions) is compacted with one ballot.
+// Small candidate windows (the host knows at most kSmallBM rows can come
+// out): one wave, no barriers (find_few_rows).
 __global__ __launch_bounds__(64) void k_mask_compact_small(const uint8_t* __restrict__ mask, int64_t win_lo,
                                                           int64_t win_hi, int64_t block, int fixed_slices,
                                                           int32_t* __restrict__ idx, int32_t* __restrict__ ctr) {
   const int lane = threadIdx.x;
-  int lo = (int)win_lo, hi = (int)win_hi;
-  if (block > 0) {
-    int first = hi;
-    for (int base = lo; base < hi; base += 64 * 16) {
-      const int p0 = base + lane * 16;
-      const unsigned fb = p0 < hi ? mask_bits16(mask, p0, hi) : 0u;
-      const int mine = fb ? p0 + __ffs(fb) - 1 : hi;
-      // lowest position over the wave: lanes cover increasing positions
-      const unsigned long long bal = __ballot(mine < hi);
-      if (bal) {
-        first = __shfl(mine, __ffsll((long long)bal) - 1);
-        break;
-      }
-    }
-    if (first >= hi) {
-      lo = hi;
-    } else {
-      const int64_t blo = win_lo + (int64_t)((first - lo) / block) * block;
-      const int64_t bhi = blo + block < (int64_t)hi ? blo + block : (int64_t)hi;
-      lo = (int)blo;
-      hi = (int)bhi;
-    }
-  }
-  const bool cand = lane < hi - lo && mask[lo + lane] != 0;  // hi - lo <= 32 here
-  const unsigned long long bal = __ballot(cand);
-  if (cand) idx[__popcll(bal & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))))] = lo + lane;
+  const FewRows f = find_few_rows(mask, win_lo, win_hi, block);
+  if (f.cand) idx[f.slot] = f.lo + lane;
   if (lane == 0) {
-    ctr[0] = __popcll(bal);
-    ctr[1] = lo;
-    ctr[2] = hi;
+    ctr[0] = f.M;
+    ctr[1] = f.lo;
+    ctr[2] = f.hi;
     ctr[3] = fixed_slices;
     ctr[4] = 1;
   }

@@ -23,20 +23,11 @@
 
 #include <math.h>
 
+#include "few_rows.h"
 #include "online_state.h"
 
 namespace dllm {
 namespace {
-
-__device__ __forceinline__ RowState shfl_xor_state(const RowState& r, int off) {
-  RowState y;
-  y.m = __shfl_xor(r.m, off);
-  y.s = __shfl_xor(r.s, off);
-  y.m2 = __shfl_xor(r.m2, off);
-  y.t = __shfl_xor(r.t, off);
-  y.a = __shfl_xor(r.a, off);
-  return y;
-}
 
 __device__ __forceinline__ uint64_t select_key(float score, int row) {
   // + 0.f maps -0 to +0, so equal scores have equal keys
@@ -260,10 +251,8 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_scatter(
 // merges every row's slices (16-byte (m, a, s, 0) records written by the
 // streaming GEMM into p.m, plus (m2, t) records in p.m2 for the extended
 // statistics; 32 lanes per row, loads issued U at a time so their
-// latencies overlap, then a butterfly), ranks each row among the rows of
-// its sequence by counting (row r precedes r' iff its score is larger, or
-// equal with the lower row = lower position) and commits each sequence's
-// first n.  A batched step (req != nullptr) has rows b * L + p.
+// latencies overlap, then a butterfly), then ranks and commits
+// (few_rows_commit).  A batched step (req != nullptr) has rows b * L + p.
 constexpr int kFinishThreads = 1024;
 static_assert(kFinishThreads == 32 * kSmallBM, "32 lanes per row");
 static_assert(kBatchMax <= kFinishThreads, "one thread per sequence");
@@ -275,9 +264,7 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish_small(const int32_t* 
                                                                 int k_stride, Partials p, Policy pol, int k,
                                                                 uint8_t* __restrict__ mask,
                                                                 int32_t* __restrict__ tokens, dllm_step_out o) {
-  __shared__ float s_conf[kSmallBM], s_lse[kSmallBM], s_score[kSmallBM], s_margin[kSmallBM], s_ent[kSmallBM];
-  __shared__ int s_tok[kSmallBM], s_seq[kSmallBM];
-  __shared__ int s_n[kBatchMax];
+  __shared__ FewRowSmem sm;
   const int M = ctr[0];
   const int slices = ctr[3];
   const int r = threadIdx.x >> 5, sub = threadIdx.x & 31;
@@ -311,63 +298,9 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish_small(const int32_t* 
     }
 #pragma unroll
     for (int off = 16; off >= 1; off >>= 1) row_merge<EXT>(st, shfl_xor_state(st, off));  // 32-lane half
-    if (sub == 0) {
-      const RowStats f = row_finish<EXT>(st);
-      s_conf[r] = f.conf;
-      s_lse[r] = f.lse;
-      s_margin[r] = f.margin;
-      s_ent[r] = f.entropy;
-      s_score[r] = policy_score(f, pol.score) + 0.f;  // -0 -> +0
-      s_tok[r] = st.a;
-      s_seq[r] = req ? (int)(idx[r] / L) : 0;
-    }
+    if (sub == 0) few_rows_set<EXT>(sm, r, st, pol.score, req ? (int)(idx[r] / L) : 0);
   }
-  __syncthreads();
-  const int t = threadIdx.x;
-  const int nseq = req ? B : 1;
-  if (t < nseq) {
-    const int Mb = req ? req[4 * t + 1] : M;
-    const int kb = req ? req[4 * t + 2] : k;
-    int n = kb < Mb ? kb : Mb;
-    if (pol.use_threshold && n > 0) {
-      int cnt = 0;
-      for (int r2 = 0; r2 < M; ++r2) cnt += (s_seq[r2] == t && s_score[r2] >= pol.tau) ? 1 : 0;
-      n = cnt < 1 ? 1 : (cnt < n ? cnt : n);
-    }
-    s_n[t] = n;
-    if (o.n_out) o.n_out[t] = n;
-    if (o.m_out) o.m_out[t] = Mb;
-  }
-  __syncthreads();
-  if (t < M) {
-    const int sq = s_seq[t];
-    const float c = s_score[t];
-    int rank = 0;
-    for (int r2 = 0; r2 < M; ++r2) {
-      const float c2 = s_score[r2];
-      rank += (s_seq[r2] == sq && (c2 > c || (c2 == c && r2 < t))) ? 1 : 0;
-    }
-    const int64_t pos_base = (int64_t)sq * L;     // 0 for a single sequence (sq == 0)
-    const int start = req ? req[4 * sq] : 0;
-    const size_t slot = req ? (size_t)pos_base + (size_t)(t - start) : (size_t)t;
-    const int g = idx[t];
-    const int pos = (int)(g - pos_base);
-    const int tok = s_tok[t];
-    if (o.row_idx) o.row_idx[slot] = pos;
-    if (o.row_tok) o.row_tok[slot] = tok;
-    if (o.row_conf) o.row_conf[slot] = s_conf[t];
-    if (o.row_lse) o.row_lse[slot] = s_lse[t];
-    if (EXT && o.row_margin) o.row_margin[slot] = s_margin[t];
-    if (EXT && o.row_entropy) o.row_entropy[slot] = s_ent[t];
-    if (rank < s_n[sq]) {
-      tokens[g] = tok;
-      mask[g] = 0;
-      const size_t sb = (size_t)sq * (size_t)k_stride + (size_t)rank;
-      if (o.sel_idx) o.sel_idx[sb] = pos;
-      if (o.sel_tok) o.sel_tok[sb] = tok;
-      if (o.sel_conf) o.sel_conf[sb] = s_conf[t];
-    }
-  }
+  few_rows_commit<EXT>(sm, M, idx, req, B, L, k_stride, pol, k, mask, tokens, o);
 }
 
 }  // namespace

@@ -151,4 +151,15 @@ __device__ __forceinline__ float policy_score(const RowStats& st, int score_kind
   return score_kind == 1 ? st.margin : (score_kind == 2 ? -st.entropy : st.conf);
 }
 
+// The state held by lane (lane ^ off) of the wave.
+__device__ __forceinline__ RowState shfl_xor_state(const RowState& r, int off) {
+  RowState y;
+  y.m = __shfl_xor(r.m, off);
+  y.s = __shfl_xor(r.s, off);
+  y.m2 = __shfl_xor(r.m2, off);
+  y.t = __shfl_xor(r.t, off);
+  y.a = __shfl_xor(r.a, off);
+  return y;
+}
+
 }  // namespace dllm

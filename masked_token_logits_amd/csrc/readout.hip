@@ -167,12 +167,15 @@ dllm_status run_step(dllm_readout* h, const StepArgs& a, const dllm::Policy& pol
     plan.fixed_slices = sl;
     plan.tile_rows = dllm::kLargeBM;
   }
-  hipError_t ce;
+  // A single-sequence few-row step has no compaction launch: the GEMM's
+  // workgroups find the candidate rows themselves.
+  const bool fused = path == kSmall && !batched && rows_max > 0;
+  hipError_t ce = hipSuccess;
   if (batched)
     ce = dllm::launch_mask_compact_batch(a.mask, a.B, a.L, *a.seqs, a.block, plan, w.idx, w.ctr, w.req, st);
-  else if (path == kSmall)
+  else if (path == kSmall && !fused)
     ce = dllm::launch_mask_compact_small(a.mask, a.win_lo, a.win_hi, a.block, plan.fixed_slices, w.idx, w.ctr, st);
-  else
+  else if (path != kSmall)
     ce = dllm::launch_mask_compact(a.mask, a.win_lo, a.win_hi, a.block, plan, w.idx, w.ctr, st);
   if (ce != hipSuccess) return DLLM_ERR_HIP;
 
@@ -182,7 +185,9 @@ dllm_status run_step(dllm_readout* h, const StepArgs& a, const dllm::Policy& pol
     hipError_t e;
     if (h->ev_before && hipEventRecord(h->ev_before, st) != hipSuccess) return DLLM_ERR_HIP;
     if (path == kSmall) {
-      e = dllm::launch_gemm_small(h->W, a.hidden, d, V, w.idx, w.ctr, plan.fixed_slices, parts, st);
+      const dllm::FindRows fr = {a.mask, a.win_lo, a.win_hi, a.block, w.idx, w.ctr};
+      e = dllm::launch_gemm_small(h->W, a.hidden, d, V, w.idx, w.ctr, plan.fixed_slices, parts,
+                                  fused ? &fr : nullptr, st);
     } else if (path == kPersistent) {
       e = dllm::launch_gemm_persistent(h->W, a.hidden, d, V, w.idx, w.ctr, h->cus, parts, st);
     } else {
@@ -191,7 +196,8 @@ dllm_status run_step(dllm_readout* h, const StepArgs& a, const dllm::Policy& pol
     if (h->log)
       fprintf(stderr, "[dllm] step B=%d rows<=%lld path=%s slices=%d cus=%d ext=%d score=%d threshold=%d\n",
               batched ? a.B : 0, (long long)rows_max,
-              path == kSmall ? "small" : path == kPersistent ? "persistent" : "streaming", plan.fixed_slices, h->cus,
+              fused ? "small-find" : path == kSmall ? "small" : path == kPersistent ? "persistent" : "streaming",
+              plan.fixed_slices, h->cus,
               (int)ext, pol.score, pol.use_threshold);
     if (e != hipSuccess) return DLLM_ERR_HIP;
     if (h->ev_after && hipEventRecord(h->ev_after, st) != hipSuccess) return DLLM_ERR_HIP;

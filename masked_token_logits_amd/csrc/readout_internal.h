@@ -113,8 +113,20 @@ struct StoreArgs {
 hipError_t launch_gemm_store(bool swiglu, const uint16_t* W, int n_w_rows, const uint16_t* X, int K, int M,
                              uint16_t* out, int ldo, int grid, hipStream_t stream);
 
+// The candidate search of a single-sequence few-row step, done by the GEMM
+// itself (every workgroup finds the same rows; workgroup 0 writes the list
+// to idx and M, lo, hi, slices, 1 to ctr[0..4] for the finish, as the
+// compaction kernel would).
+struct FindRows {
+  const uint8_t* mask;
+  int64_t win_lo, win_hi, block;
+  int32_t* idx;
+  int32_t* ctr;
+};
+
+// Few-row GEMM.  find == nullptr: rows from the compaction (idx, ctr).
 hipError_t launch_gemm_small(const uint16_t* W, const uint16_t* H, int d, int V, const int32_t* idx,
-                             const int32_t* ctr, int slices, Partials p, hipStream_t stream);
+                             const int32_t* ctr, int slices, Partials p, const FindRows* find, hipStream_t stream);
 
 // Merge + selection + commit for at most kSmallBM candidate rows, in one
 // workgroup (replaces launch_merge + launch_topk_scatter on the small path).

@@ -203,3 +203,38 @@ def test_persistent_partial_row_tiles(M):
     tokens = np.full(L, V, np.int32)
     for slices in (0, 3):
         _parity_case(H, W, mask, tokens, min(M, 20), slices=slices, where=f"M={M} slices={slices}")
+
+
+def test_few_row_steps_back_to_back():
+    """Consecutive single-sequence block steps on one handle (the GEMM finds
+    each step's rows itself): a ragged vocabulary of 40 slices, an empty
+    step (M = 0) in between, each step checked against the oracle with the
+    state carried on the device."""
+    import torch
+    rng = np.random.default_rng(21)
+    L, d, V, block, k = 160, 192, 40 * 128 - 37, 32, 3
+    H = _rand_bf16(rng, (L, d))
+    W = _rand_bf16(rng, (V, d), 0.05)
+    tokens = np.full(L, V, np.int32)
+    mask = np.zeros(L, np.uint8)
+    mask[64:] = 1
+    Wt, Ht, mt, tt = to_dev(W, H, mask, tokens)
+    rd = _readout(Wt, L, k)
+    for t in range(8):
+        lo, hi = (0, 64) if t == 3 else (64, L)  # step 3: nothing masked in the window
+        before_m, before_t = mt.cpu().numpy(), tt.cpu().numpy()
+        print(f"[case] few-row step {t} win=({lo},{hi})", flush=True)
+        g = run_step(rd, Ht, mt, tt, k, lo, hi, block)
+        o = oracle.readout_step(H, W, before_m, before_t, k, lo, hi, block)
+        where = f"few-row step {t}"
+        assert g["M"] == o.M and g["n"] == len(o.sel), where
+        np.testing.assert_array_equal(g["row_idx"], o.positions)
+        check_rows(g["row_tok"], g["row_conf"], g["row_lse"], o.stats, where)
+        band = check_selection(g["sel_idx"], o.positions, o.stats["logconf"], len(o.sel), where)
+        check_commit(before_m, before_t, g, lo, hi)
+        if band == 0:
+            np.testing.assert_array_equal(mt.cpu().numpy(), o.mask)
+        else:  # continue from the oracle's state so later steps stay comparable
+            mt.copy_(torch.from_numpy(o.mask))
+            tt.copy_(torch.from_numpy(o.tokens))
+    assert t == 7
