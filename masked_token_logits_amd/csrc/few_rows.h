@@ -86,18 +86,6 @@ struct FewRowSmem {
   int n[kBatchMax];
 };
 
-template <bool EXT>
-__device__ __forceinline__ void few_rows_set(FewRowSmem& sm, int r, const RowState& st, int score_kind, int seq) {
-  const RowStats f = row_finish<EXT>(st);
-  sm.conf[r] = f.conf;
-  sm.lse[r] = f.lse;
-  sm.margin[r] = f.margin;
-  sm.ent[r] = f.entropy;
-  sm.score[r] = policy_score(f, score_kind) + 0.f;  // -0 -> +0
-  sm.tok[r] = st.a;
-  sm.seq[r] = seq;
-}
-
 // Selection + commit of at most kSmallBM rows whose results are in `sm`
 // (every thread of the workgroup calls this; blockDim.x >= kSmallBM and
 // >= the number of sequences).  Each row is ranked among the rows of its

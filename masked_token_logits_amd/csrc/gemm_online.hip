@@ -289,6 +289,7 @@ __global__ __launch_bounds__(T::NT, T::MIN_WAVES) void k_gemm_online(const uint1
             fr.ctr[2] = f.hi;
             fr.ctr[3] = slices;
             fr.ctr[4] = 1;
+            fr.ctr[5] = 0;
           }
         }
       }

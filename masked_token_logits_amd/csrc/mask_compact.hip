@@ -250,6 +250,7 @@ __global__ __launch_bounds__(kThreads) void k_mask_compact_batch(const uint8_t* 
     ctr[2] = 0;
     ctr[3] = S;
     ctr[4] = n_rt;
+    ctr[5] = 0;
   }
 }
 

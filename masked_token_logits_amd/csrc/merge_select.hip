@@ -247,73 +247,117 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_scatter(
   }
 }
 
-// Few rows (<= kSmallBM, the semi-autoregressive block): one workgroup
-// merges every row's slices (16-byte (m, a, s, 0) records written by the
-// streaming GEMM into p.m, plus (m2, t) records in p.m2 for the extended
-// statistics; 32 lanes per row, loads issued U at a time so their
-// latencies overlap, then a butterfly), then ranks and commits
-// (few_rows_commit).  A batched step (req != nullptr) has rows b * L + p.
-constexpr int kFinishThreads = 1024;
-static_assert(kFinishThreads == 32 * kSmallBM, "32 lanes per row");
-static_assert(kBatchMax <= kFinishThreads, "one thread per sequence");
+// Few rows (<= kSmallBM, the semi-autoregressive block), one workgroup per
+// candidate row.  The row's per-slice 16-byte (m, a, s, 0) records, written
+// by the streaming GEMM into p.m (and its (m2, t) records in p.m2 for the
+// extended statistics), are loaded kFinishU per thread at a time without
+// branches (an index past the slice count re-reads the last record and is
+// merged as empty), merged in each thread, over the wave by a butterfly and
+// over the waves in wave order.  Thread 0 finishes the row and writes its
+// results to the workspace rows.  Then each workgroup counts itself in on
+// ctr[5] (zeroed by whichever kernel wrote ctr this step): thread 0's
+// agent-scope release fence orders its row writes before its atomic, and
+// the last workgroup's thread 0 acquires before the workgroup reads every
+// row back, ranks and commits (few_rows_commit).  One merge round trip on
+// kSmallBM CUs instead of the whole merge on one CU.  A batched step
+// (req != nullptr) has rows b * L + p.
+constexpr int kFinishThreads = 256;
+constexpr int kFinishU = 4;
+static_assert(kBatchMax <= kFinishThreads && kSmallBM <= kFinishThreads, "one thread per sequence and per row");
 static_assert(kTopkCap >= kSelThreads, "few-row ranking keeps the keys in sel[]");
 template <bool EXT>
-__global__ __launch_bounds__(kFinishThreads) void k_finish_small(const int32_t* __restrict__ ctr,
+__global__ __launch_bounds__(kFinishThreads) void k_finish_small(int32_t* __restrict__ ctr,
                                                                 const int32_t* __restrict__ idx,
                                                                 const int32_t* __restrict__ req, int B, int64_t L,
                                                                 int k_stride, Partials p, Policy pol, int k,
                                                                 uint8_t* __restrict__ mask,
-                                                                int32_t* __restrict__ tokens, dllm_step_out o) {
+                                                                int32_t* __restrict__ tokens, dllm_step_out o,
+                                                                FewRowResults res) {
   __shared__ FewRowSmem sm;
+  __shared__ RowState s_wave[kFinishThreads / 64];
+  __shared__ int s_last;
   const int M = ctr[0];
   const int slices = ctr[3];
-  const int r = threadIdx.x >> 5, sub = threadIdx.x & 31;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = blockIdx.x;
   if (r < M) {
     const size_t base = (size_t)r * (size_t)slices;
+    const float4* rec = reinterpret_cast<const float4*>(p.m) + base;
+    const float2* rx = reinterpret_cast<const float2*>(p.m2) + base;
     RowState st = row_state_empty();
-    constexpr int U = EXT ? 8 : 16;
-    for (int j0 = sub; j0 < slices; j0 += 32 * U) {
-      float4 rec[U];
-      float2 rx[U];
+    for (int j0 = tid; j0 < slices; j0 += kFinishThreads * kFinishU) {
+      float4 a[kFinishU];
+      float2 b[kFinishU];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int j = j0 + 32 * u;
-        rec[u] = make_float4(-INFINITY, __int_as_float(0x7FFFFFFF), 0.f, 0.f);
-        rx[u] = make_float2(-INFINITY, 0.f);
-        if (j < slices) {
-          rec[u] = reinterpret_cast<const float4*>(p.m)[base + j];
-          if (EXT) rx[u] = reinterpret_cast<const float2*>(p.m2)[base + j];
-        }
+      for (int u = 0; u < kFinishU; ++u) {
+        int j = j0 + kFinishThreads * u;
+        j = j < slices ? j : slices - 1;
+        a[u] = rec[j];
+        if (EXT) b[u] = rx[j];
       }
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
+      for (int u = 0; u < kFinishU; ++u) {
+        const bool ok = j0 + kFinishThreads * u < slices;
         RowState y;
-        y.m = rec[u].x;
-        y.a = __float_as_int(rec[u].y);
-        y.s = rec[u].z;
-        y.m2 = rx[u].x;
-        y.t = rx[u].y;
+        y.m = ok ? a[u].x : -INFINITY;
+        y.a = ok ? __float_as_int(a[u].y) : 0x7FFFFFFF;
+        y.s = ok ? a[u].z : 0.f;
+        y.m2 = (EXT && ok) ? b[u].x : -INFINITY;
+        y.t = (EXT && ok) ? b[u].y : 0.f;
         row_merge<EXT>(st, y);
       }
     }
 #pragma unroll
-    for (int off = 16; off >= 1; off >>= 1) row_merge<EXT>(st, shfl_xor_state(st, off));  // 32-lane half
-    if (sub == 0) few_rows_set<EXT>(sm, r, st, pol.score, req ? (int)(idx[r] / L) : 0);
+    for (int off = 32; off >= 1; off >>= 1) row_merge<EXT>(st, shfl_xor_state(st, off));
+    if (lane == 0) s_wave[wave] = st;
+    __syncthreads();
+    if (tid == 0) {
+#pragma unroll
+      for (int w = 1; w < kFinishThreads / 64; ++w) row_merge<EXT>(st, s_wave[w]);
+      const RowStats f = row_finish<EXT>(st);
+      res.tok[r] = st.a;
+      res.conf[r] = f.conf;
+      res.lse[r] = f.lse;
+      res.margin[r] = f.margin;
+      res.entropy[r] = f.entropy;
+    }
+  }
+  if (tid == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const bool last = atomicAdd(ctr + 5, 1) == (int)gridDim.x - 1;
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    s_last = last;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  if (tid < M) {
+    RowStats f;
+    f.conf = res.conf[tid];
+    f.lse = res.lse[tid];
+    f.margin = res.margin[tid];
+    f.entropy = res.entropy[tid];
+    sm.conf[tid] = f.conf;
+    sm.lse[tid] = f.lse;
+    sm.margin[tid] = f.margin;
+    sm.ent[tid] = f.entropy;
+    sm.score[tid] = policy_score(f, pol.score) + 0.f;  // -0 -> +0
+    sm.tok[tid] = res.tok[tid];
+    sm.seq[tid] = req ? (int)(idx[tid] / L) : 0;
   }
   few_rows_commit<EXT>(sm, M, idx, req, B, L, k_stride, pol, k, mask, tokens, o);
 }
 
 }  // namespace
 
-hipError_t launch_finish_small(const int32_t* ctr, const int32_t* idx, const int32_t* req, int B, int64_t L,
-                               int k_stride, Partials p, Policy pol, int k, uint8_t* mask, int32_t* tokens,
-                               dllm_step_out out, hipStream_t stream) {
+hipError_t launch_finish_small(int32_t* ctr, const int32_t* idx, const int32_t* req, int B, int64_t L, int k_stride,
+                               Partials p, Policy pol, int k, uint8_t* mask, int32_t* tokens, dllm_step_out out,
+                               FewRowResults res, hipStream_t stream) {
   if (p.ext)
-    hipLaunchKernelGGL(k_finish_small<true>, dim3(1), dim3(kFinishThreads), 0, stream, ctr, idx, req, B, L, k_stride,
-                       p, pol, k, mask, tokens, out);
+    hipLaunchKernelGGL(k_finish_small<true>, dim3(kSmallBM), dim3(kFinishThreads), 0, stream, ctr, idx, req, B, L,
+                       k_stride, p, pol, k, mask, tokens, out, res);
   else
-    hipLaunchKernelGGL(k_finish_small<false>, dim3(1), dim3(kFinishThreads), 0, stream, ctr, idx, req, B, L,
-                       k_stride, p, pol, k, mask, tokens, out);
+    hipLaunchKernelGGL(k_finish_small<false>, dim3(kSmallBM), dim3(kFinishThreads), 0, stream, ctr, idx, req, B, L,
+                       k_stride, p, pol, k, mask, tokens, out, res);
   return hipGetLastError();
 }
 

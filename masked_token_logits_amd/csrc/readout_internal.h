@@ -13,7 +13,8 @@ namespace dllm {
 struct Workspace {
   int32_t* idx;        // [L_max]   candidate positions, ascending (compaction output)
   int32_t* ctr;        // [16]      ctr[0] = M, ctr[1] = lo, ctr[2] = hi of the candidate window,
-                       //           ctr[3] = vocabulary slices S of this step, ctr[4] = row tiles
+                       //           ctr[3] = vocabulary slices S of this step, ctr[4] = row tiles,
+                       //           ctr[5] = arrivals of the few-row finish (zeroed with ctr[0..4])
   float* part_m;       // [part_cap] per (row, slice) running max logit
   int32_t* part_a;     // [part_cap] per (row, slice) argmax vocabulary index
   float* part_s;       // [part_cap] per (row, slice) sum of exp(z - part_m)
@@ -115,7 +116,7 @@ hipError_t launch_gemm_store(bool swiglu, const uint16_t* W, int n_w_rows, const
 
 // The candidate search of a single-sequence few-row step, done by the GEMM
 // itself (every workgroup finds the same rows; workgroup 0 writes the list
-// to idx and M, lo, hi, slices, 1 to ctr[0..4] for the finish, as the
+// to idx and M, lo, hi, slices, 1, 0 to ctr[0..5] for the finish, as the
 // compaction kernel would).
 struct FindRows {
   const uint8_t* mask;
@@ -128,13 +129,24 @@ struct FindRows {
 hipError_t launch_gemm_small(const uint16_t* W, const uint16_t* H, int d, int V, const int32_t* idx,
                              const int32_t* ctr, int slices, Partials p, const FindRows* find, hipStream_t stream);
 
-// Merge + selection + commit for at most kSmallBM candidate rows, in one
-// workgroup (replaces launch_merge + launch_topk_scatter on the small path).
-// Batched (req != nullptr): B sequences of length L, each ranked on its own;
-// outputs per sequence at b * k_stride (selection) and b * L (rows).
-hipError_t launch_finish_small(const int32_t* ctr, const int32_t* idx, const int32_t* req, int B, int64_t L,
-                               int k_stride, Partials p, Policy pol, int k, uint8_t* mask, int32_t* tokens,
-                               dllm_step_out out, hipStream_t stream);
+// Per-row results of the few-row finish (workspace rows, kSmallBM used).
+struct FewRowResults {
+  int32_t* tok;
+  float* conf;
+  float* lse;
+  float* margin;
+  float* entropy;
+};
+
+// Merge + selection + commit for at most kSmallBM candidate rows: one
+// workgroup per row, the last one to finish commits (counts on ctr[5], which
+// the kernel that wrote ctr this step has zeroed).  Replaces launch_merge +
+// launch_topk_scatter on the small path.  Batched (req != nullptr): B
+// sequences of length L, each ranked on its own; outputs per sequence at
+// b * k_stride (selection) and b * L (rows).
+hipError_t launch_finish_small(int32_t* ctr, const int32_t* idx, const int32_t* req, int B, int64_t L, int k_stride,
+                               Partials p, Policy pol, int k, uint8_t* mask, int32_t* tokens, dllm_step_out out,
+                               FewRowResults res, hipStream_t stream);
 
 hipError_t launch_merge(const int32_t* ctr, const int32_t* idx, Partials p, int score, int max_rows,
                         int32_t* row_tok, float* row_conf, float* row_lse, uint64_t* keys,
