@@ -90,7 +90,8 @@ def blas_threads() -> int:
 def kernel_source_sha(kernel_src: str) -> str:
     """sha256 over a GEMM kernel's source and the headers its code comes from."""
     h = hashlib.sha256()
-    for f in (kernel_src, os.path.join(CSRC, "readout_internal.h"), os.path.join(CSRC, "online_state.h")):
+    for f in (kernel_src, os.path.join(CSRC, "readout_internal.h"), os.path.join(CSRC, "online_state.h"),
+              os.path.join(CSRC, "few_rows.h")):
         h.update(open(f, "rb").read())
     return h.hexdigest()
 
@@ -103,13 +104,18 @@ def traffic_from_profile(workload: str, kernel_src: str):
     path = os.path.join(ROOT, "profiles", f"{stem}_{workload}_hbm_counters.md")
     if not os.path.exists(path):
         return None
-    text = open(path).read()
-    src = kernel_source_sha(kernel_src)
-    m_sha = re.search(r"source sha256:\s*([0-9a-f]{64})", text)
-    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m_sha or not m_b or m_sha.group(1) != src:
+    sha, hbm_bytes = parse_counter_summary(open(path).read())
+    if sha is None or hbm_bytes is None or sha != kernel_source_sha(kernel_src):
         return None
-    return float(m_b.group(1))
+    return hbm_bytes
+
+
+def parse_counter_summary(text: str):
+    """(source sha256, HBM bytes per launch) from a counter summary's text;
+    None for a field that is missing."""
+    m_sha = re.search(r"source sha256[^:\n]*:\s*([0-9a-f]{64})", text)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    return (m_sha.group(1) if m_sha else None), (float(m_b.group(1)) if m_b else None)
 
 
 def cpu_baseline(cfg, W, hidden_steps, mask0, tok0, n_rows_sample: int = 512):
@@ -389,10 +395,11 @@ def main(argv=None) -> int:
                     frac=round(achieved / BF16_PEAK_TFLOPS, 4))
     src = os.path.join(CSRC, "gemm_online.hip" if small else "gemm_persistent.hip")
     roof["traffic"] = None if ext else traffic_from_profile(args.workload, src)
-    if Bq > 1:
-        roof["kernel"] = "k_gemm_persistent<%s>" % ("true" if ext else "false")
-    roof["kernel"] = ("k_gemm_online<SmallTile, %s>" if small else "k_gemm_persistent<%s>") % (
-        "true" if ext else "false")
+    ext_s = "true" if ext else "false"
+    if small:  # a single sequence's GEMM also finds the candidate rows (third parameter)
+        roof["kernel"] = "k_gemm_online<SmallTile, %s, %s>" % (ext_s, "false" if Bq > 1 else "true")
+    else:
+        roof["kernel"] = "k_gemm_persistent<kEpiReadout, %s>" % ext_s
     roof["kernel_avg_us"] = round(float(gemm_ms.mean()) * 1e3, 2)
 
     value = masked_rows / elapsed

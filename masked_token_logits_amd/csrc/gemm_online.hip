@@ -139,7 +139,10 @@ __global__ __launch_bounds__(T::NT, T::MIN_WAVES) void k_gemm_online(const uint1
   // chunk instead (d % 8 == 0, so that is in bounds) and is replaced by zeros
   // when stored, so no load sits in a branch and the compiler can leave a
   // later stage's loads in flight while an earlier stage is stored.
-  auto gload_w = [&](int vt, int ks, bf16x8* ra) {
+  // `spare`: a load past the workgroup's last stage, whose data is never
+  // stored; it reads the thread's (L2-resident) first hidden row instead of
+  // W_lm, so it costs no HBM traffic.
+  auto gload_w = [&](int vt, int ks, bf16x8* ra, bool spare = false) {
     const int k0 = ks * kBK;
     const int v0 = vt * T::BN;
 #pragma unroll
@@ -148,7 +151,8 @@ __global__ __launch_bounds__(T::NT, T::MIN_WAVES) void k_gemm_online(const uint1
       v = v < V ? v : V - 1;
       int k = k0 + a_ch[i] * 8;
       k = k < d ? k : d - 8;
-      const bf16x8* src = reinterpret_cast<const bf16x8*>(W + (size_t)v * (size_t)d + k);
+      const uint16_t* row = spare ? b_ptr[0] : W + (size_t)v * (size_t)d;
+      const bf16x8* src = reinterpret_cast<const bf16x8*>(row + k);
       if constexpr (T::STREAM_W)
         ra[i] = __builtin_nontemporal_load(src);
       else
@@ -259,8 +263,12 @@ __global__ __launch_bounds__(T::NT, T::MIN_WAVES) void k_gemm_online(const uint1
     bf16x8 ra0[T::A_LD], rb0[T::B_LD], ra1[T::A_LD], rb1[T::B_LD];
     int vt = vt_lo, ks = 0;        // stage being computed
     int ld_vt = vt_lo, ld_ks = 0;  // stage being loaded
+    bool spare = false;            // the loads are past the last stage
     auto ld_next = [&]() {
-      if (ld_vt != vt_hi - 1 || ld_ks != KT - 1) next(ld_vt, ld_ks);
+      if (ld_vt != vt_hi - 1 || ld_ks != KT - 1)
+        next(ld_vt, ld_ks);
+      else
+        spare = true;
     };
     // The first two stages' W_lm loads go out before the rows are known.
     gload_w(ld_vt, ld_ks, ra0);
@@ -306,7 +314,7 @@ __global__ __launch_bounds__(T::NT, T::MIN_WAVES) void k_gemm_online(const uint1
     __syncthreads();
     int s = 0;
     for (; s + 1 < total; s += 2) {
-      gload_w(ld_vt, ld_ks, ra0);  // stage s + 2
+      gload_w(ld_vt, ld_ks, ra0, spare);  // stage s + 2
       gload_h(ld_ks, rb0);
       ld_next();
       int st_vt = vt, st_ks = ks;     // stage s + 1
@@ -316,7 +324,7 @@ __global__ __launch_bounds__(T::NT, T::MIN_WAVES) void k_gemm_online(const uint1
       __syncthreads();
       vt = st_vt;
       ks = st_ks;
-      gload_w(ld_vt, ld_ks, ra1);  // stage s + 3
+      gload_w(ld_vt, ld_ks, ra1, spare);  // stage s + 3
       gload_h(ld_ks, rb1);
       ld_next();
       next(st_vt, st_ks);             // stage s + 2
