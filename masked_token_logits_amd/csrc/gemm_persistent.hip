@@ -7,7 +7,8 @@
 //
 // MI355X mapping
 //   * One 256-thread workgroup per CU (grid = CU count), each of the 4 waves
-//     owning a 128 (rows) x 128 (vocabulary) block of the 256 x 256 tile:
+//     owning 128 rows (four interleaved 32-row blocks) x 128 vocabulary
+//     entries of the 256 x 256 tile:
 //     16 v_mfma_f32_32x32x16_bf16 per 16-deep K step, 256 fp32 accumulators
 //     per lane.  A operand = W_lm rows, B operand = gathered hidden rows, so a
 //     lane's accumulators of one 32x32 block are 16 vocabulary entries of a
@@ -149,7 +150,7 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_persistent(const uint16_t* __res
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS DMA addresses stay scalar
-  const int wr = wave >> 1;   // rows [wr * 128, +128)
+  const int wr = wave >> 1;   // row half: local 32-row blocks wr, wr + 2, wr + 4, wr + 6
   const int wv = wave & 1;    // vocabulary [wv * 128, +128)
 
   // LDS layout of a [256][32] bf16 operand tile: row r holds its four 16-byte
@@ -171,6 +172,19 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_persistent(const uint16_t* __res
     int rt, slice;
     item_coords(e, n_rt, S, rt, slice);
     const int row0 = rt * BM;
+    // Rows of the tile.  Local row l is in 32-row block l / 32; wave half wr
+    // computes local blocks wr, wr + 2, wr + 4, wr + 6, so a partial tile
+    // splits its blocks evenly between the two halves.  Readout: the n_rt
+    // tiles interleave the global 32-row blocks (tile rt holds blocks rt,
+    // rt + n_rt, ...), so the candidate rows spread evenly over the tiles
+    // (M = 288 is 5 + 4 blocks instead of 8 + 1).  Store modes: contiguous
+    // tiles.  nb = local blocks holding rows.
+    const int nblk = (M + 31) / 32;
+    const int nb = MODE == kEpiReadout ? (rt < nblk ? min(8, (nblk - rt - 1) / n_rt + 1) : 0)
+                                       : min(8, max(0, (M - row0 + 31) / 32));
+    auto grow = [&](int l) {
+      return MODE == kEpiReadout ? ((l >> 5) * n_rt + rt) * 32 + (l & 31) : row0 + l;
+    };
     const int vt_lo = (int)(((int64_t)slice * n_vt) / S);
     const int vt_hi = (int)(((int64_t)(slice + 1) * n_vt) / S);
 
@@ -181,7 +195,7 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_persistent(const uint16_t* __res
     uint32_t hoff[DMA_PER_OPERAND];
 #pragma unroll
     for (int i = 0; i < DMA_PER_OPERAND; ++i) {
-      int r = row0 + (wave + 4 * i) * DMA_ROWS + dma_row;
+      int r = grow((wave + 4 * i) * DMA_ROWS + dma_row);
       r = r < M ? r : M - 1;
       const uint32_t src = MODE == kEpiReadout ? (uint32_t)idx[r] : (uint32_t)r;
       hoff[i] = (src * (uint32_t)d + (uint32_t)(dma_chunk * 8)) * 2u;
@@ -270,11 +284,12 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_persistent(const uint16_t* __res
       if ((i & 1) == 0)
         fa[f] = *reinterpret_cast<const bf16x8*>(&lds[slot][0][0] + (wv * 128 + f * 32 + frag_row) * BK + chunk);
       else
-        fb[f] = *reinterpret_cast<const bf16x8*>(&lds[slot][1][0] + (wr * 128 + f * 32 + frag_row) * BK + chunk);
+        fb[f] = *reinterpret_cast<const bf16x8*>(&lds[slot][1][0] + ((wr + 2 * f) * 32 + frag_row) * BK + chunk);
     };
 
-    // The item's tiles for a wave whose NFR (0..4) first 32-row blocks hold
-    // candidate rows (the rest of a partial row tile is padding): MFMAs,
+    // The item's tiles for a wave whose NFR (0..4) first 32-row blocks
+    // (local blocks wr, wr + 2, ...) hold rows (the rest of a partial row
+    // tile is padding): MFMAs,
     // hidden fragment loads and the epilogue run for those blocks only,
     // while every wave issues the same DMAs and meets the same barriers.
     auto run_tiles = [&](auto nfr_tag) {
@@ -347,7 +362,7 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_persistent(const uint16_t* __res
         if constexpr (NFR > 0) {
           // Online reduction of the finished vocabulary tile, one 16-value
           // block at a time.  Accumulator x of block (fv, fr) is vocabulary
-          // entry v0 + fv*32 + 8*(x/4) + x%4 of row wr*128 + fr*32 + lane%32,
+          // entry v0 + fv*32 + 8*(x/4) + x%4 of local row (wr + 2 fr)*32 + lane%32,
           // with v0 = tile base + wv*128 + 4*(lane/32).  Within a lane the
           // index grows with (fv, x); strict '>' comparisons in that order
           // keep the lowest index among equal maxima.
@@ -396,10 +411,10 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_persistent(const uint16_t* __res
             // the last stage's waits, and the item's vmcnt(0) drains them).
             // Accumulator x of block (fv, fr) is output column
             // c0 + fv*32 + 8*(x/4) + x%4, c0 = tile base + wv*128 + 4*(lane/32),
-            // of row wr*128 + fr*32 + lane%32: four runs of 4 columns.
+            // of row row0 + (wr + 2 fr)*32 + lane%32: four runs of 4 columns.
 #pragma unroll
             for (int fr = 0; fr < NFR; ++fr) {
-              const int row = row0 + wr * 128 + fr * 32 + frag_row;
+              const int row = row0 + (wr + 2 * fr) * 32 + frag_row;
               const bool ok = row < M;
               uint16_t* orow = st.out + (size_t)(ok ? row : 0) * (size_t)st.ldo;
               if constexpr (MODE == kEpiStore) {
@@ -445,8 +460,8 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_persistent(const uint16_t* __res
         }
       }
     };
-    // 32-row blocks of this wave's 128 rows that hold candidate rows
-    const int nfr = min(4, max(0, (M - row0 - wr * 128 + 31) / 32));
+    // this wave's blocks that hold rows: local blocks wr + 2 fr < nb
+    const int nfr = min(4, max(0, (nb - wr + 1) / 2));
     switch (nfr) {
       case 4: run_tiles(std::integral_constant<int, 4>{}); break;
       case 3: run_tiles(std::integral_constant<int, 3>{}); break;
@@ -479,7 +494,7 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_persistent(const uint16_t* __res
       if (frag_half == 0) {
   #pragma unroll
         for (int fr = 0; fr < 4; ++fr) {
-          const int r = wr * 128 + fr * 32 + frag_row;
+          const int r = (wr + 2 * fr) * 32 + frag_row;
           xm[wv * BM + r] = run_m[fr];
           xa[wv * BM + r] = run_a[fr];
           xs[wv * BM + r] = run_s[fr];
@@ -504,7 +519,7 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_persistent(const uint16_t* __res
         y.m2 = EXT ? xm2[BM + r] : -INFINITY;
         y.t = EXT ? xt[BM + r] : 0.f;
         row_merge<EXT>(x, y);
-        const int row = row0 + r;
+        const int row = grow(r);  // >= M for local blocks past nb
         if (row < M) {
           const size_t o = (size_t)row * (size_t)S + (size_t)slice;
           part.m[o] = x.m;
