@@ -40,24 +40,43 @@ struct FewRows {
 
 // Called by one whole wave (lane = threadIdx.x & 63), no barrier.  Block-wise
 // (block > 0): the window is cut into blocks of `block` positions from
-// win_lo and the first one that holds a mask flag is searched 16 positions
-// per lane per iteration; its masked positions are then listed in ascending
-// order with one ballot (the host guarantees hi - lo <= kSmallBM here).
+// win_lo and the first one that holds a mask flag is searched: the first
+// 1024 positions with one 16-byte load per lane (where a semi-autoregressive
+// window normally finds its current block), the rest 64 positions per lane
+// per iteration (four loads in flight).  The block's masked positions are
+// then listed in ascending order with one ballot (the host guarantees
+// hi - lo <= kSmallBM here).
 __device__ __forceinline__ FewRows find_few_rows(const uint8_t* __restrict__ mask, int64_t win_lo, int64_t win_hi,
                                                  int64_t block) {
   const int lane = threadIdx.x & 63;
   int lo = (int)win_lo, hi = (int)win_hi;
   if (block > 0) {
     int first = hi;
-    for (int base = lo; base < hi; base += 64 * 16) {
-      const int p0 = base + lane * 16;
-      const unsigned fb = p0 < hi ? mask_bits16(mask, p0, hi) : 0u;
-      const int mine = fb ? p0 + __ffs(fb) - 1 : hi;
+    {
+      const int64_t p = (int64_t)lo + lane * 16;
+      const unsigned fb = p < hi ? mask_bits16(mask, (int)p, hi) : 0u;
+      const int mine = fb ? (int)p + __ffs(fb) - 1 : hi;
       // lowest position over the wave: lanes cover increasing positions
       const unsigned long long bal = __ballot(mine < hi);
-      if (bal) {
-        first = __shfl(mine, __ffsll((long long)bal) - 1);
-        break;
+      if (bal) first = __shfl(mine, __ffsll((long long)bal) - 1);
+    }
+    if (first >= hi) {
+      for (int64_t base = (int64_t)lo + 64 * 16; base < hi; base += 64 * 64) {  // 64-bit: no overflow near 2^31
+        unsigned fb[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int64_t p = base + lane * 64 + 16 * j;
+          fb[j] = p < hi ? mask_bits16(mask, (int)p, hi) : 0u;
+        }
+        int mine = hi;  // lowest flagged position of this lane's 64
+#pragma unroll
+        for (int j = 3; j >= 0; --j)
+          if (fb[j]) mine = (int)(base + lane * 64 + 16 * j) + __ffs(fb[j]) - 1;
+        const unsigned long long bal = __ballot(mine < hi);
+        if (bal) {
+          first = __shfl(mine, __ffsll((long long)bal) - 1);
+          break;
+        }
       }
     }
     if (first >= hi) {

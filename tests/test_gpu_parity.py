@@ -238,3 +238,20 @@ def test_few_row_steps_back_to_back():
             mt.copy_(torch.from_numpy(o.mask))
             tt.copy_(torch.from_numpy(o.tokens))
     assert t == 7
+
+
+@pytest.mark.parametrize("first", [63, 1023, 1024, 4095, 5119, 13007, 19990])
+def test_few_row_block_search_long_window(first):
+    """Block mode over a long window whose first masked position lies
+    anywhere (several search iterations, any lane and any 16-byte group of a
+    lane's 64 positions); later masked positions must not be candidates."""
+    rng = np.random.default_rng(first)
+    L, d, V, block, k = 20000, 64, 700, 32, 3
+    H = _rand_bf16(rng, (L, d))
+    W = _rand_bf16(rng, (V, d), 0.05)
+    tokens = np.full(L, V, np.int32)
+    mask = np.zeros(L, np.uint8)
+    mask[first] = 1
+    mask[first + 1:first + 40:3] = 1   # more in (and past) its block
+    mask[min(L - 1, first + 100)] = 1
+    _parity_case(H, W, mask, tokens, k, 0, L, block, where=f"long window, first={first}")
