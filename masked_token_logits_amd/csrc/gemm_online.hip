@@ -56,9 +56,11 @@ __device__ __forceinline__ int xcd_remap(int bid, int grid) {
 template <int BM_, int BN_, int WM_, int WN_, bool STREAM_W_ = false>
 struct Tile {
   static constexpr bool STREAM_W = STREAM_W_;  // W_lm read exactly once: non-temporal loads
-  // waves per SIMD to reserve registers for: the streaming tile's 40 KiB of
-  // LDS allow 4 workgroups (16 waves) per CU, so at most 128 VGPRs
-  static constexpr int MIN_WAVES = STREAM_W ? 4 : 1;
+  // waves per SIMD to reserve registers for, from the workgroups the LDS
+  // allows per CU (double-buffered W_lm and hidden stages): the streaming
+  // tile's VGPRs must not be what limits its occupancy
+  static constexpr int LDS_BYTES = 2 * (BN_ + BM_) * kBK * 2;
+  static constexpr int MIN_WAVES = STREAM_W ? (163840 / LDS_BYTES) * (WM_ * WN_) / 4 : 1;
   static constexpr int BM = BM_;             // candidate rows per workgroup
   static constexpr int BN = BN_;             // vocabulary entries per tile
   static constexpr int WM = WM_, WN = WN_;   // waves along rows / vocabulary
