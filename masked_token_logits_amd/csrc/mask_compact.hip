@@ -27,8 +27,11 @@ static_assert(kPerThread == 16, "mask_bits16 covers 16 positions");
 
 // Work plan once M is known (every thread of the workgroup calls this):
 // fixed slices, or for the persistent GEMM the slice count S minimising
-// (rounds of the grid) x (longest item), one candidate per thread, chosen
-// by an LDS atomicMin (ties: fewer slices).
+// (rounds of the grid) x (longest item), one candidate per thread (ties:
+// fewer slices).  The candidates' keys (cost << 20 | S) are reduced within
+// each wave first, so one LDS atomicMin per wave remains, and the per-thread
+// arithmetic is 32-bit: a candidate that passes the workspace check has
+// n_rt * S * tile_rows <= part_cap, so n_rt * S < 2^29 here.
 __device__ void choose_plan(int M, const PlanParams& plan, unsigned long long* s_best, int& S, int& n_rt) {
   const int tid = threadIdx.x;
   n_rt = (M + plan.tile_rows - 1) / plan.tile_rows;
@@ -36,16 +39,24 @@ __device__ void choose_plan(int M, const PlanParams& plan, unsigned long long* s
   if (S > 0) return;
   if (tid == 0) *s_best = ~0ull;
   __syncthreads();
+  unsigned long long key = ~0ull;
   if (n_rt > 0) {
     for (int c = tid + 1; c <= plan.max_slices && c <= plan.n_vt; c += blockDim.x) {
       if ((int64_t)n_rt * plan.tile_rows * c > plan.part_cap) break;
-      const int64_t items = (int64_t)n_rt * c;
-      const int64_t rounds = (items + plan.grid - 1) / plan.grid;
-      const int64_t len = (plan.n_vt + c - 1) / c;  // vocabulary tiles of the longest item
-      const unsigned long long cost = (unsigned long long)(rounds * (4 * len + 1));
-      atomicMin(s_best, (cost << 20) | (unsigned long long)c);
+      const unsigned items = (unsigned)n_rt * (unsigned)c;
+      const unsigned rounds = (items + (unsigned)plan.grid - 1u) / (unsigned)plan.grid;
+      const unsigned len = ((unsigned)plan.n_vt + (unsigned)c - 1u) / (unsigned)c;  // vocabulary tiles of the longest item
+      const unsigned long long cost = (unsigned long long)rounds * (4ull * len + 1ull);
+      const unsigned long long k = (cost << 20) | (unsigned long long)c;
+      key = k < key ? k : key;
     }
   }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const unsigned long long o = (unsigned long long)__shfl_xor((long long)key, off);
+    key = o < key ? o : key;
+  }
+  if ((tid & 63) == 0 && key != ~0ull) atomicMin(s_best, key);
   __syncthreads();
   S = (*s_best == ~0ull) ? 1 : (int)(*s_best & 0xFFFFF);
 }
