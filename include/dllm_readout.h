@@ -32,6 +32,10 @@
  *
  * Streams: all work of a step is queued on the handle's stream and the call
  * returns without waiting; the caller synchronises before reading results.
+ * A step queues kernel launches only (plus the two event records of
+ * dllm_masked_readout_set_gemm_events when set): no memset, copy, allocation
+ * or host synchronisation, so it may be captured in a HIP graph on the
+ * handle's stream; each replay is one step on the captured buffers.
  * A handle is not thread-safe; several handles may share one W_lm.
  *
  * Errors: arguments are checked on the host before anything is queued; on

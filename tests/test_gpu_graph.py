@@ -1,0 +1,82 @@
+"""A readout step captured in a HIP graph (torch.cuda.CUDAGraph) and replayed:
+a step queues kernels and nothing else (no memset, copy, allocation or
+synchronisation), so replaying it must reproduce eager steps exactly.
+Every replay is checked bit for bit against the same step run eagerly from
+the same state, with unrelated eager work and synchronisations between the
+replays.  The oracle parity of these steps is covered elsewhere; this file
+checks that capture changes nothing."""
+import numpy as np
+import pytest
+
+import workloads as WL
+from _parity import to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _rand_bf16(rng, shape, std=1.0):
+    return WL.bf16_round((rng.standard_normal(shape) * std).astype(np.float32))
+
+
+def _snapshot(out, mt, tt):
+    return {k: v.cpu().numpy().copy() for k, v in list(out.items()) + [("mask", mt), ("tokens", tt)]}
+
+
+@pytest.mark.parametrize("case", ["few_rows_block", "persistent_window", "margin_threshold"])
+def test_graph_replay_matches_eager(case):
+    import torch
+
+    import masked_token_logits_amd as mtl
+    rng = np.random.default_rng({"few_rows_block": 31, "persistent_window": 32, "margin_threshold": 33}[case])
+    L, d, V = 2048, 256, 3000
+    H = _rand_bf16(rng, (L, d))
+    W = _rand_bf16(rng, (V, d), 0.05)
+    tokens = np.full(L, V, np.int32)
+    mask = np.zeros(L, np.uint8)
+    mask[1024:] = 1
+    if case == "few_rows_block":
+        k, lo, hi, block, score, tau = 2, 1024, L, 32, "conf", None    # <= 32 rows: the few-row GEMM
+    elif case == "persistent_window":
+        k, lo, hi, block, score, tau = 24, 1024, 1536, 0, "conf", None  # up to 512 rows: persistent GEMM
+    else:
+        k, lo, hi, block, score, tau = 3, 1024, L, 32, "margin", 1e-4
+    Wt, Ht, mt0, tt0 = to_dev(W, H, mask, tokens)
+    steps = 5
+    print(f"[case] graph {case} k={k} win=({lo},{hi}) block={block} score={score} tau={tau}", flush=True)
+
+    # eager reference: `steps` consecutive steps from the initial state
+    s = torch.cuda.Stream()
+    ref = []
+    with torch.cuda.stream(s):
+        rd = mtl.MaskedReadout(Wt, L, k, stream=s)
+        out = rd.outputs()
+        init = {key: v.clone() for key, v in out.items()}
+        mt, tt = mt0.clone(), tt0.clone()
+        for _ in range(steps):
+            rd.step(Ht, mt, tt, k, lo, hi, block, out=out, score=score, tau=tau)
+            s.synchronize()
+            ref.append(_snapshot(out, mt, tt))
+
+        # the same handle, buffers reset, one step captured
+        mt.copy_(mt0)
+        tt.copy_(tt0)
+        for key, v in out.items():
+            v.copy_(init[key])
+        s.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            rd.step(Ht, mt, tt, k, lo, hi, block, out=out, score=score, tau=tau)
+        # capture queued nothing: the state is still the initial one
+        s.synchronize()
+        assert torch.equal(mt, mt0) and torch.equal(tt, tt0)
+        junk = torch.randn(1 << 20, device=mt.device)
+        for i in range(steps):
+            g.replay()
+            s.synchronize()
+            got = _snapshot(out, mt, tt)
+            for key, want in ref[i].items():
+                np.testing.assert_array_equal(got[key], want, err_msg=f"{case} replay {i} {key}")
+            junk = torch.tanh(junk * 1.0001)  # unrelated eager work between replays
+            torch.cuda.synchronize()
+    assert int(ref[-1]["m_out"][0]) >= 0
+    print(f"graph {case}: {steps} replays identical to eager steps", flush=True)
