@@ -11,13 +11,18 @@ benchmark times.
   that hold at any size check the rest (the committed set is the top n of
   the library's own confidences, and no row outside the checked set can
   reach the boundary within the tolerance).
+* The batched LLaDA-like workload (16 such sequences per step, one pass over
+  W_lm): two steps (512 and 480 candidate rows, the persistent GEMM); four
+  of the sequences against the oracle on every row, all sixteen by the
+  properties that hold at any size.
 """
 import numpy as np
 import pytest
 
 import oracle
 import workloads as WL
-from _parity import GAP, REL, check_commit, check_rank_order, check_rows, check_selection, run_step, to_dev
+from _parity import (GAP, REL, check_commit, check_rank_order, check_rows, check_selection, check_self_selection,
+                     run_batch, run_step, to_dev)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -129,3 +134,38 @@ def test_long_context_high_mask_planted():
     got = np.array([g["row_tok"][pos_to_row[p]] for p in masked_planted])
     want = np.array([planted[p] for p in masked_planted])
     np.testing.assert_array_equal(got, want)
+
+
+def test_llada_batch16_two_steps():
+    import torch
+    cfg = WL.WORKLOADS["llada_like_semi_ar_batch16"]
+    B, L = cfg.batch, cfg.L
+    W = WL.w_lm(cfg)
+    W64 = oracle.widen_bf16(W)
+    states = [WL.initial_state(cfg, b) for b in range(B)]
+    mask = np.stack([m for m, _ in states])
+    tokens = np.stack([t for _, t in states])
+    Wt, _, mt, tt = to_dev(W, np.zeros((1, cfg.d), np.uint16), mask, tokens)
+    rd = _readout(Wt, B * L, cfg.k)
+    lo, hi = cfg.win
+    seqs = [(cfg.k, lo, hi)] * B
+    for t in range(2):
+        print(f"[case] llada batch16 step {t}: generating", flush=True)
+        H = WL.hidden_batch(cfg, W, t)
+        Ht = torch.from_numpy(H.view(np.int16)).cuda()
+        before_m, before_t = mt.cpu().numpy(), tt.cpu().numpy()
+        g = run_batch(rd, Ht, mt, tt, seqs, cfg.block)
+        del Ht
+        for b in range(B):
+            where = f"batch16 step {t} seq {b}"
+            assert g[b]["M"] == 32 - 2 * t, where
+            check_self_selection(g[b], "conf", cfg.k, None, where)
+            check_commit(before_m[b], before_t[b], g[b], lo, hi)
+        for b in (0, 5, 10, 15):
+            where = f"batch16 step {t} seq {b}"
+            o = oracle.readout_step(H[b], W, before_m[b], before_t[b], cfg.k, lo, hi, cfg.block, W64=W64)
+            np.testing.assert_array_equal(g[b]["row_idx"], o.positions)
+            check_rows(g[b]["row_tok"], g[b]["row_conf"], g[b]["row_lse"], o.stats, where)
+            check_selection(g[b]["sel_idx"], o.positions, o.stats["logconf"], len(o.sel), where)
+            check_rank_order(g[b]["sel_idx"], o.positions, o.stats["logconf"], where)
+        print(f"[llada batch16] step {t} ok", flush=True)
