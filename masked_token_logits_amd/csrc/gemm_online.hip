@@ -53,13 +53,14 @@ __device__ __forceinline__ int xcd_remap(int bid, int grid) {
   return (x < rem) ? x * (per + 1) + loc : rem * (per + 1) + (x - rem) * per + loc;
 }
 
-template <int BM_, int BN_, int WM_, int WN_, bool STREAM_W_ = false>
+template <int BM_, int BN_, int WM_, int WN_, bool STREAM_W_ = false, int BK_ = kBK>
 struct Tile {
   static constexpr bool STREAM_W = STREAM_W_;  // W_lm read exactly once: non-temporal loads
   // waves per SIMD to reserve registers for, from the workgroups the LDS
   // allows per CU (double-buffered W_lm and hidden stages): the streaming
   // tile's VGPRs must not be what limits its occupancy
-  static constexpr int LDS_BYTES = 2 * (BN_ + BM_) * kBK * 2;
+  static constexpr int BK = BK_;              // K elements per LDS stage
+  static constexpr int LDS_BYTES = 2 * (BN_ + BM_) * BK * 2;
   static constexpr int MIN_WAVES = STREAM_W ? (163840 / LDS_BYTES) * (WM_ * WN_) / 4 : 1;
   static constexpr int BM = BM_;             // candidate rows per workgroup
   static constexpr int BN = BN_;             // vocabulary entries per tile
@@ -69,15 +70,19 @@ struct Tile {
   static constexpr int WV = BN / WN;         // vocabulary entries per wave
   static constexpr int FR = WR / 32;         // 32x32 MFMA blocks along rows
   static constexpr int FV = WV / 32;         // along vocabulary
-  static constexpr int CPR = kBK / 8;        // 16-byte chunks per LDS row
+  static constexpr int CPR = BK / 8;         // 16-byte chunks per LDS row
   static constexpr int A_LD = BN * CPR / NT; // W chunks per thread per stage
   static constexpr int B_LD = BM * CPR / NT; // hidden chunks per thread per stage
   static_assert(BN * CPR % NT == 0 && BM * CPR % NT == 0, "tile / thread mismatch");
   static_assert(WR % 32 == 0 && WV % 32 == 0, "wave tile must be whole MFMA blocks");
-  static_assert(CPR == 8, "swizzle assumes 8 chunks per row");
+  static_assert(CPR == 8 || CPR == 16, "swizzle: chunk ^ (row % CPR)");
 };
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * kBK + ((chunk ^ (row & 7)) << 3); }
+// LDS element offset of 16-byte chunk `chunk` of row `row` in a [rows][CPR * 8]
+// tile: chunks are XOR-swizzled by row so that the 16 consecutive rows of a
+// ds_read_b128 phase hit distinct banks.
+template <int CPR>
+__device__ __forceinline__ int swz(int row, int chunk) { return row * (CPR * 8) + ((chunk ^ (row & (CPR - 1))) << 3); }
 
 template <class T, bool EXT, bool FIND>
 __global__ __launch_bounds__(T::NT, T::MIN_WAVES) void k_gemm_online(const uint16_t* __restrict__ W,
@@ -86,8 +91,8 @@ __global__ __launch_bounds__(T::NT, T::MIN_WAVES) void k_gemm_online(const uint1
                                                        const int32_t* __restrict__ ctr, int slices,
                                                        int n_vt, Partials part, FindRows fr) {
   static_assert(!FIND || (T::STREAM_W && T::BM == kSmallBM), "the row search is the few-row tile's");
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][T::BN * kBK];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][T::BM * kBK];
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][T::BN * T::BK];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][T::BM * T::BK];
 
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int rt = bid / slices;
@@ -106,7 +111,7 @@ __global__ __launch_bounds__(T::NT, T::MIN_WAVES) void k_gemm_online(const uint1
   const int wave = tid >> 6;
   const int wr = wave / T::WN;  // wave row group
   const int wv = wave % T::WN;  // wave vocabulary group
-  const int KT = (d + kBK - 1) / kBK;
+  const int KT = (d + T::BK - 1) / T::BK;
 
   // Per-thread load assignments (fixed for the workgroup's life).
   int a_row[T::A_LD], a_ch[T::A_LD];
@@ -145,7 +150,7 @@ __global__ __launch_bounds__(T::NT, T::MIN_WAVES) void k_gemm_online(const uint1
   // stored; it reads the thread's (L2-resident) first hidden row instead of
   // W_lm, so it costs no HBM traffic.
   auto gload_w = [&](int vt, int ks, bf16x8* ra, bool spare = false) {
-    const int k0 = ks * kBK;
+    const int k0 = ks * T::BK;
     const int v0 = vt * T::BN;
 #pragma unroll
     for (int i = 0; i < T::A_LD; ++i) {
@@ -162,7 +167,7 @@ __global__ __launch_bounds__(T::NT, T::MIN_WAVES) void k_gemm_online(const uint1
     }
   };
   auto gload_h = [&](int ks, bf16x8* rb) {
-    const int k0 = ks * kBK;
+    const int k0 = ks * T::BK;
 #pragma unroll
     for (int i = 0; i < T::B_LD; ++i) {
       int k = k0 + b_ch[i] * 8;
@@ -171,13 +176,13 @@ __global__ __launch_bounds__(T::NT, T::MIN_WAVES) void k_gemm_online(const uint1
     }
   };
   auto lstore = [&](int buf, int ks, const bf16x8* ra, const bf16x8* rb) {
-    const int k0 = ks * kBK;
+    const int k0 = ks * T::BK;
 #pragma unroll
     for (int i = 0; i < T::A_LD; ++i)
-      *reinterpret_cast<bf16x8*>(&sA[buf][swz(a_row[i], a_ch[i])]) = k0 + a_ch[i] * 8 < d ? ra[i] : zero8;
+      *reinterpret_cast<bf16x8*>(&sA[buf][swz<T::CPR>(a_row[i], a_ch[i])]) = k0 + a_ch[i] * 8 < d ? ra[i] : zero8;
 #pragma unroll
     for (int i = 0; i < T::B_LD; ++i)
-      *reinterpret_cast<bf16x8*>(&sB[buf][swz(b_row[i], b_ch[i])]) = k0 + b_ch[i] * 8 < d ? rb[i] : zero8;
+      *reinterpret_cast<bf16x8*>(&sB[buf][swz<T::CPR>(b_row[i], b_ch[i])]) = k0 + b_ch[i] * 8 < d ? rb[i] : zero8;
   };
 
   f32x16 acc[T::FV][T::FR];
@@ -199,18 +204,18 @@ __global__ __launch_bounds__(T::NT, T::MIN_WAVES) void k_gemm_online(const uint1
   // tile's last K stage the online reduction of the tile.
   auto body = [&](int buf, int vt, int ks) {
 #pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
+    for (int kk = 0; kk < T::BK / 16; ++kk) {
       const int ch = kk * 2 + frag_half;
       bf16x8 fa[T::FV], fb[T::FR];
 #pragma unroll
       for (int fv = 0; fv < T::FV; ++fv) {
         const int r = wv * T::WV + fv * 32 + frag_row;
-        fa[fv] = *reinterpret_cast<const bf16x8*>(&sA[buf][swz(r, ch)]);
+        fa[fv] = *reinterpret_cast<const bf16x8*>(&sA[buf][swz<T::CPR>(r, ch)]);
       }
 #pragma unroll
       for (int fr = 0; fr < T::FR; ++fr) {
         const int r = wr * T::WR + fr * 32 + frag_row;
-        fb[fr] = *reinterpret_cast<const bf16x8*>(&sB[buf][swz(r, ch)]);
+        fb[fr] = *reinterpret_cast<const bf16x8*>(&sB[buf][swz<T::CPR>(r, ch)]);
       }
 #pragma unroll
       for (int fv = 0; fv < T::FV; ++fv)
@@ -439,7 +444,7 @@ using LargeTile = Tile<kLargeBM, kLargeBN, 2, 4>;
 // streamed with non-temporal loads (no L2 / Infinity Cache allocation):
 // measured 180 -> 162 us per step on the LLaDA-like head.
 using SmallTile = Tile<kSmallBM, kSmallBN, 1, 4, true>;
-static_assert(kSmallBM + 1 <= SmallTile::BM * kBK / 2, "candidate list must fit in sB[1]");
+static_assert(kSmallBM + 1 <= SmallTile::BM * SmallTile::BK / 2, "candidate list must fit in sB[1]");
 
 }  // namespace
 
