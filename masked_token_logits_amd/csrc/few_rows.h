@@ -2,8 +2,8 @@
 // current block of semi-autoregressive decoding (Sparse-dLLM, Experiment
 // "Memory": logits only for the current block).  The candidate search is
 // shared by the one-wave compaction kernel and the few-row GEMM (which, for
-// a single sequence, finds its rows itself); the finish and commit by the
-// few-row finish kernels.
+// a single sequence, finds its rows itself); the selection and commit is
+// the last step of the few-row finish kernel.
 #pragma once
 
 #include "online_state.h"

@@ -202,7 +202,7 @@ dllm_status run_step(dllm_readout* h, const StepArgs& a, const dllm::Policy& pol
     if (e != hipSuccess) return DLLM_ERR_HIP;
     if (h->ev_after && hipEventRecord(h->ev_after, st) != hipSuccess) return DLLM_ERR_HIP;
     if (path == kSmall) {
-      // merge, selection and commit of <= 32 rows in one workgroup
+      // merge (one workgroup per row), selection and commit of <= 32 rows
       const dllm::FewRowResults res = {w.row_tok, w.row_conf, w.row_lse, w.row_margin, w.row_entropy};
       if (dllm::launch_finish_small(w.ctr, w.idx, req, a.B, a.L, k_stride, parts, pol, a.k, a.mask, a.tokens, o,
                                     res, st) != hipSuccess)
