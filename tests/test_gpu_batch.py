@@ -173,3 +173,27 @@ def test_batch_matches_single_sequence_steps():
         n = len(o[b].sel)
         if n == 0 or n == len(srt) or srt[n - 1] - srt[n] > 1e-3:
             assert set(g[b]["sel_idx"].tolist()) == set(s["sel_idx"].tolist())
+
+
+def test_batch_compaction_window_lengths():
+    """Windows of 1024 positions and less are compacted from one load per
+    lane, longer ones by re-reading passes: block mode on both sides of the
+    boundary, a long window whose first masked block lies far in, one with
+    none, and an unblocked window just above the boundary."""
+    B, L, d, V = 5, 3000, 64, 900
+    H, W, _, _ = _inputs(63, B, L, d, V, 0.0, spread=False)
+    rng = np.random.default_rng(64)
+    mask = np.zeros((B, L), np.uint8)
+    mask[0, 700:1024] = rng.random(324) < 0.5          # window [0, 1024): one load
+    mask[1, 1010:1030] = 1                               # window [0, 1025): passes; first block at 992
+    mask[2, 2601:2700] = rng.random(99) < 0.6            # window [0, 3000): first block far in
+    mask[2, 2600] = 1
+    mask[4, 100:1100] = rng.random(1000) < 0.03          # unblocked window [100, 1125)
+    tokens = np.full((B, L), V, np.int32)
+    seqs = [(3, 0, 1024), (2, 0, 1025), (4, 0, 3000), (2, 0, 3000), (40, 100, 1125)]
+    Wt, Ht, mt, tt = to_dev(W, H, mask, tokens)
+    rd = _readout(Wt, B * L, 40)
+    for block in (32, 0):
+        print(f"[case] batch compaction window lengths block={block}", flush=True)
+        g = run_batch(rd, Ht, mt.clone(), tt.clone(), seqs, block)
+        _check_batch(g, H, W, mask, tokens, seqs, block, where=f"window lengths block={block}")
