@@ -17,8 +17,11 @@ llada_b16 workload decodes 16 such sequences together in one batched step
 per denoising step (they share W_lm's single pass).
 
 Prints ONE JSON line: masked tokens/s, the GEMM kernel's roofline (HIP
-events around its launch on the library's stream), and the fp64 CPU
-oracle timed on a bounded sample of the same workload.  ``--score`` and
+events around its launch on the library's stream), the per-step latency
+(median and p95, from a second pass), plain-torch readouts that materialise
+the logits (all L rows, or only the candidate rows) timed and sized on the
+same state, and the fp64 CPU oracle timed on a bounded sample of the same
+workload.  ``--score`` and
 ``--tau`` time another selection policy (ranking by top-2 margin or negative
 entropy, whose statistics the GEMM then also accumulates; threshold commits
 with cap k) instead of the default top-k by confidence.  ``--workload ffn``
@@ -240,6 +243,63 @@ def bench_ffn(args, name: str) -> int:
     return 0
 
 
+def torch_logits_baseline(cfg, Ht, Wt, mask_dev, reps: int = 5, cap_bytes: float = 48e9):
+    """Plain-torch readouts that materialise the logits, timed on the first
+    denoising step's state for the memory and time comparison.  'full' runs
+    the LM head over all L positions; 'mask_only' runs it over the window's
+    candidate rows only, with no streaming.  Both then take the softmax,
+    each row's maximum and top-k over the candidates.  The candidate list is
+    built once, outside the timing.  A variant is not run when its logits
+    would need more than `cap_bytes` (bf16 + fp32 logits + fp32
+    probabilities) or hold 2^31 elements or more; its size is reported."""
+    import torch
+    lo, hi = cfg.win
+    pos = torch.nonzero(mask_dev[lo:hi]).flatten() + lo
+    if cfg.block and pos.numel():
+        b0 = lo + ((int(pos[0]) - lo) // cfg.block) * cfg.block
+        pos = pos[pos < b0 + cfg.block]
+    M = int(pos.numel())
+    n = min(cfg.k, M)
+    H = Ht.view(torch.bfloat16)
+    W = Wt.view(torch.bfloat16)
+
+    def readout(rows):
+        P = torch.softmax((rows @ W.t()).float(), dim=-1)
+        return P.max(dim=-1)
+
+    def full():
+        conf, _ = readout(H)
+        return torch.topk(conf[pos], n).indices
+
+    def mask_only():
+        conf, _ = readout(H[pos])
+        return torch.topk(conf, n).indices
+
+    res = {"rows": {"full": cfg.L, "mask_only": M}, "k": n, "reps": reps}
+    for name, fn, rows in (("full", full, cfg.L), ("mask_only", mask_only, M)):
+        need = rows * cfg.V * 10
+        if M == 0 or need > cap_bytes or rows * cfg.V >= 2**31:
+            res[name] = {"not_run": f"{rows} x {cfg.V} logits, ~{need / 1e9:.0f} GB" if M else "no candidates"}
+            continue
+        fn()  # warm-up (library handles, allocator)
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        times = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        times.sort()
+        res[name] = {"ms_per_step": round(times[len(times) // 2], 4),
+                     "transient_bytes": int(torch.cuda.max_memory_allocated() - base)}
+    torch.cuda.empty_cache()
+    return res
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -346,6 +406,27 @@ def main(argv=None) -> int:
     elapsed = time.perf_counter() - t0
     log(f"[bench] timed {args.steps} steps in {elapsed * 1e3:.2f} ms")
 
+    # Per-step latency, in a separate pass after the timed region: events
+    # around each step on the library's stream (torch's current stream), the
+    # state resets left outside them.
+    mtl.dllm_masked_readout_set_gemm_events(rd.handle, None, None)
+    lat = []
+    for j in range(args.steps):
+        t = (total + j) % cfg.steps
+        if t == 0:
+            mt.copy_(m_pristine)
+            tt.copy_(t_pristine)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        if Bq > 1:
+            rd.step_batch(Hts[t], mt, tt, seqs, cfg.block, score=args.score, tau=args.tau)
+        else:
+            rd.step(Hts[t], mt, tt, cfg.k, lo, hi, cfg.block, score=args.score, tau=args.tau)
+        b.record(stream)
+        lat.append((a, b))
+    torch.cuda.synchronize()
+    lat_us = np.sort(np.array([a.elapsed_time(b) for a, b in lat]) * 1e3)
+
     Ms = m_slots.cpu().numpy().astype(np.int64).sum(axis=1)   # candidate rows per step, all sequences
     timed_M = Ms[args.warmup:]
     masked_rows = int(timed_M.sum())
@@ -425,12 +506,24 @@ def main(argv=None) -> int:
             "masked_rows_timed": masked_rows,
             "peak_mem_bytes": peak_mem,
             "full_logits_fp32_bytes": cfg.L * V * 4,
+            "mask_only_logits_fp32_bytes": int(timed_M.max()) * V * 4,
             "workspace_bytes": int(rd.workspace.numel()),
             "parallelism": "single GPU",
             "policy": {"score": args.score, "threshold": args.tau},
         },
         "roofline": roof,
+        "latency": {
+            "median_us": round(float(np.percentile(lat_us, 50)), 2),
+            "p95_us": round(float(np.percentile(lat_us, 95)), 2),
+            "steps": int(lat_us.size),
+            "how": "HIP events around each step on the library's stream, in a pass after the timed region",
+        },
     }
+    if Bq == 1:
+        log("[bench] timing plain-torch readouts that materialise the logits")
+        mt.copy_(m_pristine)
+        rec["torch_logits_baseline"] = torch_logits_baseline(cfg, Hts[0], Wt, mt)
+        rec["torch_logits_baseline"]["streamed_transient_bytes"] = int(rd.workspace.numel())
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         if Bq > 1:
