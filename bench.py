@@ -318,8 +318,8 @@ def main(argv=None) -> int:
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the readout would shard W_lm by vocabulary or the rows by sequence; see the design notes).",
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(the readout would shard W_lm by vocabulary, or the rows by sequence).",
               file=sys.stderr)
         return 2
 
