@@ -307,6 +307,8 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--workload", choices=sorted(WORKLOADS) + sorted(FFN_WORKLOADS), default="llada")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
+    ap.add_argument("--no-torch-baseline", action="store_true",
+                    help="skip the plain-torch logits readouts (e.g. under a profiler)")
     ap.add_argument("--slices", type=int, default=0, help="force the GEMM's vocabulary slice count")
     ap.add_argument("--score", choices=["conf", "margin", "neg_entropy"], default="conf",
                     help="ranking score of the selection (default: confidence)")
@@ -519,7 +521,7 @@ def main(argv=None) -> int:
             "how": "HIP events around each step on the library's stream, in a pass after the timed region",
         },
     }
-    if Bq == 1:
+    if Bq == 1 and not args.no_torch_baseline:
         log("[bench] timing plain-torch readouts that materialise the logits")
         mt.copy_(m_pristine)
         rec["torch_logits_baseline"] = torch_logits_baseline(cfg, Hts[0], Wt, mt)
