@@ -44,6 +44,38 @@ from ._abi import (  # noqa: F401
 )
 
 
+_BF16_DTYPES = ("bfloat16", "int16", "uint16")   # bf16 data or its bit pattern
+_OUT_INT = ("n_out", "m_out", "sel_idx", "sel_tok", "row_idx", "row_tok")
+_OUT_FLOAT = ("sel_conf", "row_conf", "row_lse", "row_margin", "row_entropy")
+
+
+def _check(t, name: str, dtypes, shape=None, min_numel=None, device=None):
+    """Host-side guard before a raw pointer crosses the C ABI: the kernels
+    read and write exactly the documented extents, so a wrong dtype, shape,
+    stride or device would be an out-of-bounds access on the GPU.  Raw
+    integers (device addresses) are passed through unchecked."""
+    if isinstance(t, int):
+        return
+    if str(t.dtype).replace("torch.", "") not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} is not one of {', '.join(dtypes)}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError(f"{name}: {t.numel()} elements, at least {min_numel} needed")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+
+
+def _check_out(out, n_scalar: int, n_sel: int, n_rows: int, device) -> None:
+    for key, v in (out or {}).items():
+        if key not in _OUT_INT and key not in _OUT_FLOAT:
+            raise KeyError(f"unknown output {key!r}")
+        need = n_scalar if key in ("n_out", "m_out") else n_sel if key.startswith("sel_") else n_rows
+        _check(v, key, ("int32",) if key in _OUT_INT else ("float32",), min_numel=need, device=device)
+
+
 class SwiGLUFFN:
     """The sequence-chunked SwiGLU FFN: packed gate/up weights, W_down and
     a torch-allocated [chunk, F] activation workspace.
@@ -54,6 +86,12 @@ class SwiGLUFFN:
     def __init__(self, W_gate, W_up, W_down, chunk: int, stream=None):
         import torch
         F, d = W_gate.shape
+        dev = W_gate.device
+        _check(W_gate, "W_gate", _BF16_DTYPES, shape=(F, d))
+        _check(W_up, "W_up", _BF16_DTYPES, shape=(F, d), device=dev)
+        _check(W_down, "W_down", _BF16_DTYPES, shape=(d, F), device=dev)
+        if not W_gate.is_cuda:
+            raise ValueError("W_gate must be a device tensor")
         self.F, self.d, self.chunk = int(F), int(d), int(chunk)
         self.stream = stream if stream is not None else torch.cuda.current_stream(W_gate.device)
         self.W_gu = torch.empty((2 * self.F, self.d), dtype=W_gate.dtype, device=W_gate.device)
@@ -69,8 +107,11 @@ class SwiGLUFFN:
     def __call__(self, X, Y=None):
         """Queue Y = FFN(X) (X [L, d]); returns Y (new unless given; may be X)."""
         import torch
+        dev = self.W_gu.device
+        _check(X, "X", _BF16_DTYPES, shape=(X.shape[0], self.d), device=dev)
         if Y is None:
             Y = torch.empty_like(X)
+        _check(Y, "Y", _BF16_DTYPES, shape=tuple(X.shape), device=dev)
         st = dllm_ffn_swiglu_chunked(X, int(X.shape[0]), self.d, self.W_gu, self.W_down, self.F, self.chunk, Y,
                                      self.workspace, int(self.workspace.numel()), self.stream)
         if st != DLLM_OK:
@@ -86,6 +127,9 @@ class MaskedReadout:
 
     def __init__(self, W_lm, L_max: int, k_max: int, stream=None):
         import torch
+        if W_lm.dim() != 2:
+            raise ValueError("W_lm must be [V, d]")
+        _check(W_lm, "W_lm", _BF16_DTYPES)
         if not W_lm.is_cuda:
             raise ValueError("W_lm must be a device tensor")
         V, d = W_lm.shape
@@ -135,6 +179,11 @@ class MaskedReadout:
         L = int(hidden.shape[0])
         if win_hi is None:
             win_hi = L
+        dev = self.W_lm.device
+        _check(hidden, "hidden", _BF16_DTYPES, shape=(L, self.d), device=dev)
+        _check(mask, "mask", ("uint8", "bool"), shape=(L,), device=dev)
+        _check(tokens, "tokens", ("int32",), shape=(L,), device=dev)
+        _check_out(out, 1, int(k), max(int(win_hi) - int(win_lo), 0), dev)
         if score == "conf" and tau is None:
             st = dllm_masked_readout_step(self.handle, hidden, L, mask, tokens, int(k), int(win_lo),
                                           int(win_hi), int(block), out)
@@ -170,6 +219,11 @@ class MaskedReadout:
         B, L = int(hidden.shape[0]), int(hidden.shape[1])
         if len(seqs) != B:
             raise ValueError("one (k, win_lo, win_hi) per sequence")
+        dev = self.W_lm.device
+        _check(hidden, "hidden", _BF16_DTYPES, shape=(B, L, self.d), device=dev)
+        _check(mask, "mask", ("uint8", "bool"), shape=(B, L), device=dev)
+        _check(tokens, "tokens", ("int32",), shape=(B, L), device=dev)
+        _check_out(out, B, B * max(self.k_max, 1), B * L, dev)
         pol = None if (score == "conf" and tau is None) else make_policy(score, tau)
         st = dllm_masked_readout_step_batch(self.handle, B, hidden, L, mask, tokens, seqs, int(block), pol, out)
         if st != DLLM_OK:
