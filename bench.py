@@ -121,6 +121,18 @@ def parse_counter_summary(text: str):
     return (m_sha.group(1) if m_sha else None), (float(m_b.group(1)) if m_b else None)
 
 
+def cpu_model() -> str | None:
+    """The host CPU's model name (Linux /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(cfg, W, hidden_steps, mask0, tok0, n_rows_sample: int = 512):
     """The fp64 oracle as it stands, on a bounded sample of the workload."""
     import numpy as np
@@ -151,7 +163,7 @@ def cpu_baseline(cfg, W, hidden_steps, mask0, tok0, n_rows_sample: int = 512):
         sample = f"first {rows} masked rows of the step, full V each (rows/s scaled to masked tokens/s)"
     dt = time.perf_counter() - t0
     return dict(value=rows / dt, unit="masked tokens/s", cores=blas_threads(), kind="oracle",
-                sample=sample, seconds=round(dt, 3))
+                sample=sample, seconds=round(dt, 3), cpu=cpu_model())
 
 
 def cpu_baseline_ffn(cfg, X, Wg, Wu, Wd, budget_s: float = 10.0):
@@ -167,7 +179,7 @@ def cpu_baseline_ffn(cfg, X, Wg, Wu, Wd, budget_s: float = 10.0):
     dt = time.perf_counter() - t0
     return dict(value=rows / dt, unit="tokens/s", cores=blas_threads(), kind="oracle",
                 sample=f"first {rows} rows of the sequence, blocks of 512 (fp64 gate/up/down GEMMs)",
-                seconds=round(dt, 3))
+                seconds=round(dt, 3), cpu=cpu_model())
 
 
 def bench_ffn(args, name: str) -> int:

@@ -22,3 +22,9 @@ def test_counter_summary_parser_rejects_missing_fields():
     sha = "ab" * 32
     text = f"source sha256 (over the four files, in that order): {sha}\nhbm_bytes_per_launch: 1.5e9\n"
     assert bench.parse_counter_summary(text) == (sha, 1.5e9)
+
+
+def test_cpu_model_is_a_string_or_none():
+    import bench
+    m = bench.cpu_model()
+    assert m is None or (isinstance(m, str) and m)
