@@ -8,8 +8,10 @@
 // the exclusive prefix of the per-thread counts comes from ballots of the
 // count's bits (count = sum_b 2^b * bit_b, so the prefix is
 // sum_b 2^b * popcount(ballot(bit_b) & lanes-below)), across the 16 waves
-// from a small LDS table.  M and the window actually used go to ctr[0..2]
-// so no host synchronisation is needed before the next kernel.
+// from a small LDS table.  Each chunk's positions are placed in LDS at
+// those offsets and stored to idx as one contiguous run.  M and the window
+// actually used go to ctr[0..2] so no host synchronisation is needed before
+// the next kernel.
 //
 // The same kernel then fixes how the GEMM splits the work, now that M is
 // known (choose_plan).  A batched step compacts every sequence's window
@@ -134,6 +136,7 @@ __global__ __launch_bounds__(kThreads) void k_mask_compact(const uint8_t* __rest
   __shared__ int s_first;
   __shared__ unsigned long long s_best;
   __shared__ int s_wave_total[kThreads / 64];
+  __shared__ int s_pos[kChunk];  // one chunk's positions, in order, for coalesced stores
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -185,14 +188,18 @@ __global__ __launch_bounds__(kThreads) void k_mask_compact(const uint8_t* __rest
       wave_off += (w < wave) ? t : 0;
       total += t;
     }
-    int out = running + wave_off + pre;
+    // Each lane's positions go to LDS at its prefix, then the chunk's list
+    // leaves in consecutive 4-byte stores across the workgroup.
+    int out = wave_off + pre;
     while (bits) {
       const int j = __ffs(bits) - 1;
       bits &= bits - 1;
-      idx[out++] = p0 + j;
+      s_pos[out++] = p0 + j;
     }
+    __syncthreads();
+    for (int i = tid; i < total; i += kThreads) idx[running + i] = s_pos[i];
     running += total;
-    __syncthreads();  // s_wave_total is rewritten by the next chunk
+    __syncthreads();  // s_wave_total and s_pos are rewritten by the next chunk
   }
   const int M = running;
   int S, n_rt;
