@@ -135,6 +135,30 @@ def test_identical_rows_commit_lowest_positions():
     assert len(set(g["row_conf"].tolist())) == 1
 
 
+@pytest.mark.parametrize("k", [50, 700, 1500])
+def test_identical_rows_radix_select(k):
+    """More than 1024 candidates (the radix-select path) in two groups of
+    bit-identical rows: every key shares its score bytes with a third or two
+    thirds of the others, so the selection is decided by the row bits alone.
+    The commit must be the rows in (score descending, position ascending)
+    order, exactly."""
+    rng = np.random.default_rng(40 + k)
+    L, d, V = 3000, 64, 700
+    ra, rb = _rand_bf16(rng, d), _rand_bf16(rng, d)
+    H = np.where((np.arange(L) % 3 == 0)[:, None], rb[None, :], ra[None, :]).astype(ra.dtype)
+    W = _rand_bf16(rng, (V, d), 0.05)
+    mask = (rng.random(L) < 0.7).astype(np.uint8)
+    tokens = np.full(L, V, np.int32)
+    print(f"[case] identical rows radix k={k} M={int(mask.sum())}", flush=True)
+    g, o, _, _ = _parity_case(H, W, mask, tokens, k, where=f"identical radix k={k}")
+    assert g["M"] > 1024
+    pos = np.flatnonzero(mask)
+    conf = g["row_conf"][: g["M"]]
+    assert len(set(conf.tolist())) == 2
+    order = sorted(range(len(pos)), key=lambda i: (-float(conf[i]), int(pos[i])))
+    assert list(g["sel_idx"]) == [int(pos[i]) for i in order[:k]]
+
+
 def test_argmax_ties_lowest_vocab_index():
     """Duplicate W_lm rows give bit-identical logits; the lowest index must win
     across lanes, tiles and slices."""
