@@ -150,7 +150,9 @@ size_t dllm_masked_readout_workspace_bytes(int64_t L_max, int64_t d, int64_t V, 
  *   stream     hipStream_t to queue work on (NULL = the default stream)
  * Host-only: makes no HIP call and queues no work (the device's compute-unit
  * count is queried by the first step, which returns DLLM_ERR_HIP if there is
- * no usable device).
+ * no usable device).  With the environment variable DLLM_LOG=1 when the
+ * handle is created, each of its steps prints the GEMM variant it chose
+ * to stderr.
  */
 dllm_status dllm_masked_readout_create(dllm_readout **out, const uint16_t *W_lm, int64_t V,
                                        int64_t d, int64_t L_max, int32_t k_max,
