@@ -177,19 +177,39 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_scatter(
         if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
       }
       __syncthreads();
-      if (tid == 0) {
-        int cum = 0, digit = 0;
-        for (int dg = 255; dg >= 0; --dg) {
-          const int c = (int)hist[dg];
-          if (cum + c >= remaining) {
-            digit = dg;
-            break;
-          }
-          cum += c;
+      if (tid < 64) {
+        // The digit holding the remaining-th largest key, searched by one
+        // wave: lane l holds digits 255 - 4l - j (j = 0..3, descending), a
+        // prefix over the lanes gives the keys above each lane's digits, and
+        // the one lane where the count crosses `remaining` (1 <= remaining
+        // <= keys with this prefix) picks the digit.
+        int c4[4], sum = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          c4[j] = (int)hist[255 - 4 * tid - j];
+          sum += c4[j];
         }
-        s_digit = digit;
-        s_remaining = remaining - cum;
-        s_done = (s_remaining == (int)hist[digit]) ? 1 : 0;
+        int incl = sum;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int y = __shfl_up(incl, off);
+          if (tid >= off) incl += y;
+        }
+        const int excl = incl - sum;
+        if (excl < remaining && incl >= remaining) {
+          int cum = excl, digit = 255 - 4 * tid - 3;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if (cum + c4[j] >= remaining) {
+              digit = 255 - 4 * tid - j;
+              break;
+            }
+            cum += c4[j];
+          }
+          s_digit = digit;
+          s_remaining = remaining - cum;
+          s_done = (s_remaining == (int)hist[digit]) ? 1 : 0;
+        }
       }
       __syncthreads();
       prefix |= (uint64_t)s_digit << shift;
