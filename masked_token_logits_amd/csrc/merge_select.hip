@@ -78,6 +78,7 @@ __global__ __launch_bounds__(kMergeWaves * 64) void k_merge(const int32_t* __res
 }
 
 constexpr int kSelThreads = 1024;
+constexpr int kSelU = 4;  // keys per thread loaded together in the radix passes
 
 // One workgroup per sequence (a single sequence: one workgroup over all rows).
 // The sequence's rows are [start, start + M) of the compacted list; keys hold
@@ -172,9 +173,18 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_scatter(
       const int shift = 56 - 8 * pass;
       for (int i = tid; i < 256; i += kSelThreads) hist[i] = 0;
       __syncthreads();
-      for (int i = tid; i < M; i += kSelThreads) {
-        const uint64_t key = kb[i];
-        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      // kSelU keys per thread in flight before their histogram updates
+      for (int base = 0; base < M; base += kSelU * kSelThreads) {
+        uint64_t kk[kSelU];
+#pragma unroll
+        for (int u = 0; u < kSelU; ++u) {
+          const int i = base + u * kSelThreads + tid;
+          kk[u] = i < M ? kb[i] : ~prefix;  // a key that cannot match the prefix
+        }
+#pragma unroll
+        for (int u = 0; u < kSelU; ++u)
+          if ((kk[u] & pmask) == prefix && base + u * kSelThreads + tid < M)
+            atomicAdd(&hist[(kk[u] >> shift) & 255u], 1u);
       }
       __syncthreads();
       if (tid < 64) {
