@@ -179,7 +179,7 @@ __global__ __launch_bounds__(kSelThreads) void k_topk_scatter(
 #pragma unroll
         for (int u = 0; u < kSelU; ++u) {
           const int i = base + u * kSelThreads + tid;
-          kk[u] = i < M ? kb[i] : ~prefix;  // a key that cannot match the prefix
+          kk[u] = i < M ? kb[i] : 0;  // past M: skipped by the bound check below
         }
 #pragma unroll
         for (int u = 0; u < kSelU; ++u)
