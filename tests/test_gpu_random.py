@@ -72,3 +72,25 @@ def test_random_batch_step(seed):
     print(f"[case] random batch {seed} B={B} L={L} d={d} V={V} block={block} score={score} tau={tau}", flush=True)
     g = run_batch(rd, Ht, mt, tt, seqs, block, score=score, tau=tau, ext=True)
     _check_batch(g, H, W, mask, tokens, seqs, block, score=score, tau=tau, where=f"random batch {seed}")
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_ffn(seed):
+    """The chunked SwiGLU FFN on random legal shapes (d % 256 == 0,
+    F % 128 == 0), chunk sizes from 1 row to more than L, in place or not,
+    held to the FFN tests' error bounds."""
+    from test_gpu_ffn import RMS_REL, _bf, _check, _run
+    import workloads as WL
+    r = np.random.default_rng(3000 + seed)
+    L = int(r.integers(1, 1500))
+    d = 256 * int(r.integers(1, 5))
+    F = 128 * int(r.integers(1, 13))
+    chunk = int(r.integers(1, 2001)) if r.random() < 0.8 else int(r.integers(1, 9))
+    inplace = r.random() < 0.3
+    rng = np.random.default_rng(4000 + seed)
+    X = WL.bf16_round(rng.standard_normal((L, d)).astype(np.float32))
+    Wg, Wu, Wd = _bf(rng, (F, d), 0.05), _bf(rng, (F, d), 0.05), _bf(rng, (d, F), 0.05)
+    print(f"[case] random ffn {seed} L={L} d={d} F={F} chunk={chunk} inplace={inplace}", flush=True)
+    Yg, _ = _run(X, Wg, Wu, Wd, chunk, "inplace" if inplace else None)
+    rel = _check(Yg, X, Wg, Wu, Wd, where=f"random ffn {seed}")
+    assert rel < RMS_REL
