@@ -240,3 +240,14 @@ def test_policy_slice_invariance():
         np.testing.assert_array_equal(g["row_tok"], ref["row_tok"])
         np.testing.assert_allclose(g["row_margin"], ref["row_margin"], rtol=1e-4, atol=1e-7)
         np.testing.assert_allclose(g["row_entropy"], ref["row_entropy"], rtol=1e-5, atol=1e-6)
+
+
+@pytest.mark.parametrize("score,tau", [("conf", None), ("margin", 0.05)])
+def test_largest_k(score, tau):
+    """k = k_max = 4096, the largest the library accepts, with about 6400
+    candidates: the selection holds 4096 winners in LDS and sorts them."""
+    import masked_token_logits_amd as mtl
+    k = mtl.DLLM_K_MAX_LIMIT
+    H, W, mask, tokens = _inputs(77, 8000, 64, 500, 0.8)
+    g, o, _ = _policy_case(H, W, mask, tokens, k, score=score, tau=tau, where=f"k=4096 {score} {tau}")
+    assert g["M"] > k
