@@ -279,3 +279,19 @@ def test_few_row_block_search_long_window(first):
     mask[first + 1:first + 40:3] = 1   # more in (and past) its block
     mask[min(L - 1, first + 100)] = 1
     _parity_case(H, W, mask, tokens, k, 0, L, block, where=f"long window, first={first}")
+
+
+@pytest.mark.parametrize("first", [65535, 131000])
+def test_few_row_block_search_longest_context(first):
+    """The in-GEMM block search over a 131072-position window (the
+    long-context length), with the first masked position mid-window or near
+    its end."""
+    rng = np.random.default_rng(first)
+    L, d, V, block, k = 131072, 32, 300, 32, 2
+    H = _rand_bf16(rng, (L, d))
+    W = _rand_bf16(rng, (V, d), 0.05)
+    tokens = np.full(L, V, np.int32)
+    mask = np.zeros(L, np.uint8)
+    mask[first] = 1
+    mask[first + 2:min(L, first + 60):5] = 1
+    _parity_case(H, W, mask, tokens, k, 0, L, block, where=f"longest window, first={first}")
