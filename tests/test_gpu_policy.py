@@ -251,3 +251,16 @@ def test_largest_k(score, tau):
     H, W, mask, tokens = _inputs(77, 8000, 64, 500, 0.8)
     g, o, _ = _policy_case(H, W, mask, tokens, k, score=score, tau=tau, where=f"k=4096 {score} {tau}")
     assert g["M"] > k
+
+
+@pytest.mark.parametrize("V", [2, 7, 31])
+@pytest.mark.parametrize("path", sorted(PATHS))
+def test_small_vocabulary(path, V):
+    """Vocabularies smaller than one 32-wide MFMA block: every vocabulary
+    tile is mostly padding, whose rows are clamped on load and whose logits
+    are dropped; all three scores, and a threshold on the margin."""
+    _, L, d, _, frac, lo, hi, block, k = PATHS[path]
+    H, W, mask, tokens = _inputs(V + L, L, d, V, frac)
+    for score, tau in (("conf", None), ("margin", None), ("neg_entropy", None), ("margin", 0.2)):
+        _policy_case(H, W, mask, tokens, k, lo, hi, block, score=score, tau=tau,
+                     where=f"V={V} {path} {score} {tau}")
