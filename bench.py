@@ -2,31 +2,38 @@
 """Benchmark of the masked-token readout on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--workload llada|llada_b16|tiny|dream|lc_low|lc_high|ffn|ffn_tiny]
+                    [--workload all|tiny|llada|dream|lc_low|lc_high|llada_b16|ffn|ffn_tiny]
                     [--score conf|margin|neg_entropy] [--tau T]
 
 A step is one denoising readout (compaction, masked LM-head GEMM with the
 streaming vocabulary reduction, merge, top-k commit) over one synthetic
-batch.  The default workload is the LLaDA-8B-like head (L=4096, d=4096,
-V=126464) decoded semi-autoregressively: the last 1024 positions are masked,
-blocks of 32, k=2 per step, 32 consecutive steps with the mask/token state
-carried on the device and the hidden states re-drawn every step; after 32
-steps the state is reset from a pristine device copy (inside the timed
-region).  All inputs are resident in HBM before timing starts.  The
-llada_b16 workload decodes 16 such sequences together in one batched step
-per denoising step (they share W_lm's single pass).
+batch, with all inputs resident in HBM before timing starts.
 
-Prints ONE JSON line: masked tokens/s, the GEMM kernel's roofline (HIP
-events around its launch on the library's stream), the per-step latency
-(median and p95, from a second pass), plain-torch readouts that materialise
-the logits (all L rows, or only the candidate rows) timed and sized on the
-same state, and the fp64 CPU oracle timed on a bounded sample of the same
-workload.  ``--score`` and
-``--tau`` time another selection policy (ranking by top-2 margin or negative
-entropy, whose statistics the GEMM then also accumulates; threshold commits
-with cap k) instead of the default top-k by confidence.  ``--workload ffn``
-times the sequence-chunked SwiGLU FFN of one layer over the 128k-context
-LLaDA-like sequence (chunks of 8192 rows) instead of the readout.
+The default (``--workload all``) runs the five seeded workloads one after
+the other and prints ONE JSON line whose headline is the long-context
+high-mask step (L=131072, d=4096, V=126464, M=117965 masked rows, 5% planted
+rows, k=1024), the largest single-GPU workload and the one whose LM-head
+GEMM is MFMA-bound; the other four (tiny; LLaDA-like semi-AR loop;
+Dream-like; long-context low-mask) are nested under ``configs``, each with
+its own throughput, roofline, per-step latency, transient device memory and
+CPU-oracle baseline.  ``--workload NAME`` runs one workload alone.
+
+The LLaDA-like loop decodes the last 1024 positions in blocks of 32, k=2 per
+step, 32 consecutive steps with the mask/token state carried on the device
+and the hidden states re-drawn every step; after 32 steps the state is reset
+from a pristine device copy (inside the timed region).  llada_b16 decodes 16
+such sequences together in one batched step (one pass over W_lm).
+
+Per workload: masked tokens/s, the GEMM kernel's roofline (HIP events around
+its launch on the library's stream), the per-step latency (median and p95,
+from a second pass), device memory (resident before the step, the step's
+transient peak above it, against the fp32 logits of all L rows and of the M
+candidate rows), plain-torch readouts that materialise the logits, and the
+fp64 CPU oracle timed on a bounded sample.  ``--score`` and ``--tau`` time
+another selection policy (ranking by top-2 margin or negative entropy, whose
+statistics the GEMM then also accumulates; threshold commits with cap k).
+``--workload ffn`` times the sequence-chunked SwiGLU FFN of one layer over
+the 128k-context LLaDA-like sequence (chunks of 8192 rows) instead.
 """
 from __future__ import annotations
 
@@ -81,13 +88,22 @@ class Hip:
         self.lib.hipEventDestroy(C.c_void_p(e))
 
 
-def blas_threads() -> int:
+def cpu_share() -> tuple[int, int]:
+    """(threads the CPU oracle leg uses, cores visible to this process).
+
+    The oracle uses every visible core, but no more than the process's CPU
+    share when the environment states one (OMP_NUM_THREADS): on a host whose
+    cores are shared between GPUs the affinity mask can show far more cores
+    than one GPU's share."""
     try:
-        from threadpoolctl import threadpool_info
-        n = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
-        return max(n) if n else 1
-    except Exception:  # pragma: no cover
-        return 1
+        visible = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        visible = os.cpu_count() or 1
+    share = os.environ.get("OMP_NUM_THREADS", "")
+    n = visible
+    if share.isdigit() and int(share) > 0:
+        n = min(n, int(share))
+    return max(1, n), visible
 
 
 def kernel_source_sha(kernel_src: str) -> str:
@@ -122,67 +138,99 @@ def parse_counter_summary(text: str):
 
 
 def cpu_model() -> str | None:
-    """The host CPU's model name (Linux /proc/cpuinfo), or None."""
+    """The host CPU's model name from /proc/cpuinfo, with its family, model
+    and stepping numbers (a virtual machine may report only the vendor's
+    product line as the name), or None."""
+    info = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if ":" not in line:
+                    if info:
+                        break
+                    continue
+                key, val = (s.strip() for s in line.split(":", 1))
+                info.setdefault(key, val)
     except OSError:
-        pass
-    return None
+        return None
+    name = info.get("model name")
+    if name is None:
+        return None
+    ids = [f"{k} {info[k]}" for k in ("cpu family", "model", "stepping") if k in info]
+    return f"{name} ({', '.join(ids)})" if ids else name
 
 
-def cpu_baseline(cfg, W, hidden_steps, mask0, tok0, n_rows_sample: int = 512):
-    """The fp64 oracle as it stands, on a bounded sample of the workload."""
+def _oracle_threads(n: int):
+    """Context manager pinning the BLAS pool to n threads (threadpoolctl)."""
+    try:
+        from threadpoolctl import threadpool_limits
+        return threadpool_limits(limits=n, user_api="blas")
+    except Exception:  # pragma: no cover
+        import contextlib
+        return contextlib.nullcontext()
+
+
+def cpu_baseline(cfg, W, hidden_steps, mask0, tok0, budget_s: float = 6.0):
+    """The fp64 oracle as it stands, on a bounded sample of the workload,
+    with BLAS pinned to this process's cores.  The one-off fp64 widening of
+    W_lm is timed apart (setup_seconds) and not counted."""
     import numpy as np
 
     import oracle
-    t0 = time.perf_counter()
-    W64 = oracle.widen_bf16(W)
-    if cfg.steps > 1:
-        rows = passes = 0
-        while passes < 10 and (passes == 0 or time.perf_counter() - t0 < 10.0):
-            mask, tok = mask0, tok0
-            for t in range(cfg.steps):
-                lo, hi = cfg.win
-                r = oracle.readout_step(hidden_steps[t], W, mask, tok, cfg.k, lo, hi, cfg.block, W64=W64)
-                rows += r.M
-                mask, tok = r.mask, r.tokens
-            passes += 1
-        sample = (f"{passes} x all {cfg.steps} steps of the semi-AR pass ({rows} masked rows, full V each; "
-                  f"W_lm widened to fp64 once)")
-    elif cfg.L * cfg.V <= 8 * 1024 * 1024:
-        r = oracle.readout_step(hidden_steps[0], W, mask0, tok0, cfg.k, W64=W64)
-        rows = r.M
-        sample = f"the whole step ({rows} masked rows)"
-    else:
-        pos = np.flatnonzero(mask0)[:n_rows_sample]
-        oracle.readout_rows(hidden_steps[0], W, pos, W64=W64)
-        rows = len(pos)
-        sample = f"first {rows} masked rows of the step, full V each (rows/s scaled to masked tokens/s)"
-    dt = time.perf_counter() - t0
-    return dict(value=rows / dt, unit="masked tokens/s", cores=blas_threads(), kind="oracle",
-                sample=sample, seconds=round(dt, 3), cpu=cpu_model())
+    threads, visible = cpu_share()
+    with _oracle_threads(threads):
+        t_setup = time.perf_counter()
+        W64 = oracle.widen_bf16(W)
+        setup = time.perf_counter() - t_setup
+        t0 = time.perf_counter()
+        if cfg.steps > 1:
+            rows = passes = 0
+            while passes < 10 and (passes == 0 or time.perf_counter() - t0 < budget_s):
+                mask, tok = mask0, tok0
+                for t in range(cfg.steps):
+                    lo, hi = cfg.win
+                    r = oracle.readout_step(hidden_steps[t], W, mask, tok, cfg.k, lo, hi, cfg.block, W64=W64)
+                    rows += r.M
+                    mask, tok = r.mask, r.tokens
+                passes += 1
+            sample = f"{passes} x all {cfg.steps} steps of the semi-AR pass ({rows} masked rows, full V each)"
+        elif cfg.L * cfg.V <= 8 * 1024 * 1024:
+            r = oracle.readout_step(hidden_steps[0], W, mask0, tok0, cfg.k, W64=W64)
+            rows = r.M
+            sample = f"the whole step ({rows} masked rows)"
+        else:
+            # consecutive blocks of the step's masked rows until the budget is spent
+            pos = np.flatnonzero(mask0)
+            rows = 0
+            while rows < len(pos) and (rows == 0 or time.perf_counter() - t0 < budget_s):
+                oracle.readout_rows(hidden_steps[0], W, pos[rows:rows + 256], W64=W64)
+                rows = min(rows + 256, len(pos))
+            sample = (f"first {rows} of the step's {len(pos)} masked rows, full V each "
+                      f"(rows/s scaled to masked tokens/s)")
+        dt = time.perf_counter() - t0
+    return dict(value=rows / dt, unit="masked tokens/s", cores=threads, kind="oracle", sample=sample,
+                seconds=round(dt, 3), setup_seconds=round(setup, 3), visible_cores=visible, cpu=cpu_model())
 
 
 def cpu_baseline_ffn(cfg, X, Wg, Wu, Wd, budget_s: float = 10.0):
     """The fp64 FFN oracle as it stands, on consecutive blocks of rows until
     about ``budget_s`` seconds have passed."""
     import oracle
-    t0 = time.perf_counter()
-    rows = 0
-    while rows < cfg.L and (rows == 0 or time.perf_counter() - t0 < budget_s):
-        n = min(512, cfg.L - rows)
-        oracle.ffn_rows(X[rows:rows + n], Wg, Wu, Wd)
-        rows += n
-    dt = time.perf_counter() - t0
-    return dict(value=rows / dt, unit="tokens/s", cores=blas_threads(), kind="oracle",
+    threads, visible = cpu_share()
+    with _oracle_threads(threads):
+        t0 = time.perf_counter()
+        rows = 0
+        while rows < cfg.L and (rows == 0 or time.perf_counter() - t0 < budget_s):
+            n = min(512, cfg.L - rows)
+            oracle.ffn_rows(X[rows:rows + n], Wg, Wu, Wd)
+            rows += n
+        dt = time.perf_counter() - t0
+    return dict(value=rows / dt, unit="tokens/s", cores=threads, kind="oracle",
                 sample=f"first {rows} rows of the sequence, blocks of 512 (fp64 gate/up/down GEMMs)",
-                seconds=round(dt, 3), cpu=cpu_model())
+                seconds=round(dt, 3), visible_cores=visible, cpu=cpu_model())
 
 
-def bench_ffn(args, name: str) -> int:
+def bench_ffn(args, name: str) -> dict:
     """One FFN layer over the whole sequence per step."""
     import numpy as np
     import torch
@@ -251,8 +299,7 @@ def bench_ffn(args, name: str) -> int:
         rec["cpu_baseline"] = cpu_baseline_ffn(cfg, X, Wg, Wu, Wd)
     else:
         rec["cpu_baseline"] = None
-    print(json.dumps(rec), flush=True)
-    return 0
+    return rec
 
 
 def torch_logits_baseline(cfg, Ht, Wt, mask_dev, reps: int = 5, cap_bytes: float = 48e9):
@@ -312,52 +359,16 @@ def torch_logits_baseline(cfg, Ht, Wt, mask_dev, reps: int = 5, cap_bytes: float
     return res
 
 
-def main(argv=None) -> int:
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=320)
-    ap.add_argument("--warmup", type=int, default=32)
-    ap.add_argument("--workload", choices=sorted(WORKLOADS) + sorted(FFN_WORKLOADS), default="llada")
-    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
-    ap.add_argument("--no-torch-baseline", action="store_true",
-                    help="skip the plain-torch logits readouts (e.g. under a profiler)")
-    ap.add_argument("--slices", type=int, default=0, help="force the GEMM's vocabulary slice count")
-    ap.add_argument("--score", choices=["conf", "margin", "neg_entropy"], default="conf",
-                    help="ranking score of the selection (default: confidence)")
-    ap.add_argument("--tau", type=float, default=None,
-                    help="threshold commits (score >= tau, at least 1, at most k) instead of top-k")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="only run a plain 1 GiB device copy 3 times (reference for HBM byte counters)")
-    args = ap.parse_args(argv)
-
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: the library has no multi-GPU path "
-              "(the readout would shard W_lm by vocabulary, or the rows by sequence).",
-              file=sys.stderr)
-        return 2
-
+def bench_readout(args, short: str) -> dict:
+    """One readout workload: the timed steps, then the latency pass, the
+    torch readouts and the CPU oracle.  Returns its record."""
     import numpy as np
     import torch
 
     import masked_token_logits_amd as mtl
     import workloads as WL
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        return 2
-    if args.copy_calibration:
-        x = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
-        y = torch.empty_like(x)
-        for _ in range(3):
-            y.copy_(x)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_calibration_bytes": 1 << 30, "copies": 3}))
-        return 0
-    mtl.load()
-    if args.workload in FFN_WORKLOADS:
-        return bench_ffn(args, FFN_WORKLOADS[args.workload])
-    cfg = WL.WORKLOADS[WORKLOADS[args.workload]]
+    cfg = WL.WORKLOADS[WORKLOADS[short]]
     dev = torch.device("cuda", 0)
     t_gen = time.perf_counter()
     W = WL.w_lm(cfg)
@@ -374,15 +385,12 @@ def main(argv=None) -> int:
         h = WL.hidden_batch(cfg, W, t) if Bq > 1 else WL.hidden(cfg, W, t)[0]
         Hts.append(torch.from_numpy(h.view(np.int16)).to(dev))
         hidden_steps.append(None if Bq > 1 else h)
-    log(f"[bench] generated {args.workload} inputs in {time.perf_counter() - t_gen:.1f}s")
+    log(f"[bench] {short}: generated inputs in {time.perf_counter() - t_gen:.1f}s")
 
     m_pristine = torch.from_numpy(mask0).to(dev)
     t_pristine = torch.from_numpy(tok0).to(dev)
     mt = m_pristine.clone()
     tt = t_pristine.clone()
-    torch.cuda.synchronize()
-    torch.cuda.reset_peak_memory_stats()
-
     stream = torch.cuda.current_stream(dev)
     rd = mtl.MaskedReadout(Wt, cfg.L * Bq, cfg.k, stream=stream)
     if args.slices:
@@ -393,6 +401,11 @@ def main(argv=None) -> int:
     seqs = [(cfg.k, lo, hi)] * Bq
     hip = Hip()
     ev = [(hip.event(), hip.event()) for _ in range(args.steps)]
+    # everything a step reads or writes is allocated now: the peak above this
+    # is the step's own transient memory
+    torch.cuda.synchronize()
+    resident = int(torch.cuda.memory_allocated())
+    torch.cuda.reset_peak_memory_stats()
 
     def one(i: int, timed_index: int | None) -> None:
         t = i % cfg.steps
@@ -418,7 +431,7 @@ def main(argv=None) -> int:
         one(args.warmup + j, j)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    log(f"[bench] timed {args.steps} steps in {elapsed * 1e3:.2f} ms")
+    log(f"[bench] {short}: timed {args.steps} steps in {elapsed * 1e3:.2f} ms")
 
     # Per-step latency, in a separate pass after the timed region: events
     # around each step on the library's stream (torch's current stream), the
@@ -440,6 +453,7 @@ def main(argv=None) -> int:
         lat.append((a, b))
     torch.cuda.synchronize()
     lat_us = np.sort(np.array([a.elapsed_time(b) for a, b in lat]) * 1e3)
+    peak = int(torch.cuda.max_memory_allocated())
 
     Ms = m_slots.cpu().numpy().astype(np.int64).sum(axis=1)   # candidate rows per step, all sequences
     timed_M = Ms[args.warmup:]
@@ -448,18 +462,17 @@ def main(argv=None) -> int:
     for a, b in ev:
         hip.destroy(a)
         hip.destroy(b)
-    peak_mem = int(torch.cuda.max_memory_allocated())
 
     d, V = cfg.d, cfg.V
     ext = args.score != "conf"
     small = Bq * (min(cfg.block, hi - lo) if cfg.block else hi - lo) <= 32
     rec_bytes = 24 if ext else 16
     slices = (V + 127) // 128
+    flops = 2.0 * timed_M * d * V
     if Bq > 1:
         # Batched steps range from HBM-bound (few rows: W_lm's stream) to
         # MFMA-bound (many rows).  The bound is the one that takes longer at
         # the published peaks over the timed steps; both figures are kept.
-        flops = 2.0 * timed_M * d * V
         bytes_per = V * d * 2 + timed_M * d * 2 + timed_M * 4   # W_lm once, the rows, the row outputs
         t_mfma = float(flops.sum()) / (BF16_PEAK_TFLOPS * 1e12)
         t_hbm = float(bytes_per.sum()) / (HBM_PEAK_GBS * 1e9)
@@ -483,24 +496,25 @@ def main(argv=None) -> int:
         achieved = float(bytes_per.sum()) / (gemm_ms.sum() * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4))
+        roof["mfma_tflops"] = round(float(flops.sum()) / (gemm_ms.sum() * 1e-3) / 1e12, 2)
     else:
-        flops = 2.0 * timed_M * d * V
         achieved = float(flops.sum()) / (gemm_ms.sum() * 1e-3) / 1e12
         roof = dict(bound="mfma", achieved=round(achieved, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
                     frac=round(achieved / BF16_PEAK_TFLOPS, 4))
     src = os.path.join(CSRC, "gemm_online.hip" if small else "gemm_persistent.hip")
-    roof["traffic"] = None if ext else traffic_from_profile(args.workload, src)
+    roof["traffic"] = None if ext else traffic_from_profile(short, src)
     ext_s = "true" if ext else "false"
     if small:  # a single sequence's GEMM also finds the candidate rows (third parameter)
         roof["kernel"] = "k_gemm_online<SmallTile, %s, %s>" % (ext_s, "false" if Bq > 1 else "true")
     else:
         roof["kernel"] = "k_gemm_persistent<kEpiReadout, %s>" % ext_s
     roof["kernel_avg_us"] = round(float(gemm_ms.mean()) * 1e3, 2)
+    roof["algorithmic_flops_per_step"] = float(flops.mean())
 
-    value = masked_rows / elapsed
+    M_max = int(timed_M.max())
     rec = {
         "metric": "masked tokens/sec per denoise step",
-        "value": round(value, 1),
+        "value": round(masked_rows / elapsed, 1),
         "unit": "masked tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -517,13 +531,20 @@ def main(argv=None) -> int:
                         + (f", {Bq} sequences per batched step" if Bq > 1 else "") + ")",
             "batch": Bq,
             "L": cfg.L, "d": d, "V": V, "k": cfg.k,
+            "masked_rows_per_step_max": M_max,
             "masked_rows_timed": masked_rows,
-            "peak_mem_bytes": peak_mem,
-            "full_logits_fp32_bytes": cfg.L * V * 4,
-            "mask_only_logits_fp32_bytes": int(timed_M.max()) * V * 4,
-            "workspace_bytes": int(rd.workspace.numel()),
             "parallelism": "single GPU",
             "policy": {"score": args.score, "threshold": args.tau},
+        },
+        "memory": {
+            "resident_before_step_bytes": resident,
+            "peak_bytes": peak,
+            "step_transient_bytes": peak - resident,
+            "workspace_bytes": int(rd.workspace.numel()),
+            "full_logits_fp32_bytes": cfg.L * Bq * V * 4,
+            "mask_only_logits_fp32_bytes": M_max * V * 4,
+            "how": "torch.cuda.max_memory_allocated over the timed and latency passes, minus the memory "
+                   "allocated before the first step (W_lm, hidden states, mask/tokens, workspace)",
         },
         "roofline": roof,
         "latency": {
@@ -534,12 +555,16 @@ def main(argv=None) -> int:
         },
     }
     if Bq == 1 and not args.no_torch_baseline:
-        log("[bench] timing plain-torch readouts that materialise the logits")
+        log(f"[bench] {short}: timing plain-torch readouts that materialise the logits")
         mt.copy_(m_pristine)
         rec["torch_logits_baseline"] = torch_logits_baseline(cfg, Hts[0], Wt, mt)
-        rec["torch_logits_baseline"]["streamed_transient_bytes"] = int(rd.workspace.numel())
+        rec["torch_logits_baseline"]["streamed_transient_bytes"] = peak - resident
+    rd.close()
+    del Hts, Wt, mt, tt, m_pristine, t_pristine, m_slots, rd
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle on a bounded sample")
+        log(f"[bench] {short}: timing the CPU oracle on a bounded sample")
         if Bq > 1:
             # the oracle steps each sequence on its own: time sequence 0's pass
             hs0 = [WL.hidden(cfg, W, t, seq=0)[0] for t in range(cfg.steps)]
@@ -549,8 +574,78 @@ def main(argv=None) -> int:
             rec["cpu_baseline"] = cpu_baseline(cfg, W, hidden_steps, mask0, tok0)
     else:
         rec["cpu_baseline"] = None
+    return rec
+
+
+# The five seeded workloads of the default run, in order; the last is the headline.
+ALL_ORDER = ("tiny", "llada", "dream", "lc_low", "lc_high")
+NESTED_DROP = ("metric", "n_gpus", "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "steps", "warmup")
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", choices=["all"] + sorted(WORKLOADS) + sorted(FFN_WORKLOADS), default="all")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
+    ap.add_argument("--no-torch-baseline", action="store_true",
+                    help="skip the plain-torch logits readouts (e.g. under a profiler)")
+    ap.add_argument("--slices", type=int, default=0, help="force the GEMM's vocabulary slice count")
+    ap.add_argument("--score", choices=["conf", "margin", "neg_entropy"], default="conf",
+                    help="ranking score of the selection (default: confidence)")
+    ap.add_argument("--tau", type=float, default=None,
+                    help="threshold commits (score >= tau, at least 1, at most k) instead of top-k")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy 3 times (reference for HBM byte counters)")
+    args = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(the readout would shard W_lm by vocabulary, or the rows by sequence).",
+              file=sys.stderr)
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import masked_token_logits_amd as mtl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    if args.copy_calibration:
+        x = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": 1 << 30, "copies": 3}))
+        return 0
+    mtl.load()
+    if args.workload in FFN_WORKLOADS:
+        rec = bench_ffn(args, FFN_WORKLOADS[args.workload])
+    elif args.workload != "all":
+        rec = bench_readout(args, args.workload)
+    else:
+        recs = {}
+        for short in ALL_ORDER:
+            recs[short] = bench_readout(args, short)
+            r = recs[short]
+            log(f"[bench] {short}: {r['value']:.1f} masked tok/s, {r['roofline']['bound']} frac "
+                f"{r['roofline']['frac']}")
+        rec = dict(recs[ALL_ORDER[-1]])
+        rec["configs"] = {}
+        for short in ALL_ORDER:
+            nested = {k: v for k, v in recs[short].items() if k not in NESTED_DROP}
+            rec["configs"][WORKLOADS[short]] = nested
+        rec["config"] = dict(rec["config"])
+        rec["config"]["headline"] = ("the largest single-GPU workload, MFMA-bound; the other four are nested "
+                                     "under 'configs' with their own roofline, latency, memory and CPU baseline")
     print(json.dumps(rec), flush=True)
-    rd.close()
     return 0
 
 
