@@ -93,6 +93,30 @@ def test_row_stats_brute_force():
     assert st["tok"][4] == 10 and st["gap2"][4] == 0.0
 
 
+def test_readout_rows_chunks_match_brute_force():
+    """The chunked readout (row_chunk = 7 over 23 unsorted positions: three
+    full chunks and a ragged one) gives per position exactly the pure-Python
+    readout of its exact logits (math.fsum of exact bf16 products), in the
+    order the positions were given, and bit for bit what one chunk gives."""
+    rng = np.random.default_rng(17)
+    L, d, V = 40, 16, 50
+    H = _rand_bf16(rng, (L, d))
+    W = _rand_bf16(rng, (V, d), std=0.5)
+    pos = rng.permutation(L)[:23]
+    st7 = oracle.readout_rows(H, W, pos, row_chunk=7)
+    st1 = oracle.readout_rows(H, W, pos, row_chunk=1000)
+    for key in st1:
+        assert np.array_equal(st7[key], st1[key]), key
+    Hf = oracle.widen_bf16(H)
+    Wf = oracle.widen_bf16(W)
+    for i, p in enumerate(pos):
+        z = [math.fsum(float(a) * float(b) for a, b in zip(Hf[p], Wf[v])) for v in range(V)]
+        b = _brute_row(z)
+        assert st7["tok"][i] == b["tok"], i
+        for key in ("mx", "conf", "lse", "margin", "entropy"):
+            assert st7[key][i] == pytest.approx(b[key], rel=1e-12, abs=1e-12), (i, key)
+
+
 def test_zero_row_closed_form():
     for V in (1, 2, 7, 4096):
         st = oracle.row_stats(np.zeros((1, V)))
