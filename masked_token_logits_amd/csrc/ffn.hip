@@ -6,7 +6,7 @@
 // so the FFN's transient memory is chunk * F * 2 bytes instead of the
 // L * F-sized gate, up and activation tensors (Mosaic, Fig. 3: the FFN peak
 // at low mask ratio).
-#include "../../include/dllm_ffn.h"
+#include "dllm_ffn.h"
 #include "readout_internal.h"
 
 namespace dllm {
