@@ -227,6 +227,37 @@ dllm_status dllm_masked_readout_step_batch(dllm_readout *h, int32_t B, const uin
                                            int64_t block, const dllm_policy *policy,
                                            const dllm_step_out *out);
 
+/* Size of the library's static device scratch, per GPU (see below). */
+#define DLLM_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/*
+ * One readout step with no handle and no workspace argument, for callers
+ * that cannot allocate device memory or create a workspace: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Arguments and results are those of dllm_masked_readout_create followed by
+ * dllm_masked_readout_step_ex with L_max = L and k_max = k (same checks, same
+ * kernels, same results).  Instead of a caller workspace the step uses a
+ * static device array of DLLM_NOALLOC_SCRATCH_BYTES that the library holds
+ * on every GPU it runs on until the process ends; the call itself allocates
+ * nothing (no hipMalloc, no allocating library routine).
+ *   stream   hipStream_t to queue the step on (NULL = the default stream);
+ *            the call returns without waiting, like dllm_masked_readout_step
+ * The first call on a device, with that device current, looks up the
+ * array's device address (hipGetSymbolAddress) and keeps it.
+ * Limits: DLLM_ERR_WORKSPACE when dllm_masked_readout_workspace_bytes(L, d,
+ * V, k) exceeds DLLM_NOALLOC_SCRATCH_BYTES (at V = 126464 about L <= 25000);
+ * k <= DLLM_K_MAX_LIMIT.  Nothing is queued on an error.
+ * Concurrency: every call on one GPU uses that GPU's one scratch array, and
+ * the array keeps the last call's contents (each step writes what it reads
+ * first, so stale contents do not matter).  Calls whose work overlaps in
+ * time on one GPU -- on different streams or from different host threads --
+ * race on the array; queue them on one stream (or otherwise serialise them).
+ */
+dllm_status dllm_masked_readout_step_noalloc(const uint16_t *W_lm, int64_t V, int64_t d, const uint16_t *hidden,
+                                             int64_t L, uint8_t *mask, int32_t *tokens, int32_t k,
+                                             int64_t win_lo, int64_t win_hi, int64_t block,
+                                             const dllm_policy *policy, const dllm_step_out *out, void *stream);
+
 /* Free the host handle (no device memory is owned).  NULL -> DLLM_OK. */
 dllm_status dllm_masked_readout_destroy(dllm_readout *h);
 

@@ -18,6 +18,7 @@ from ._abi import (  # noqa: F401
     DLLM_ERR_UNSUPPORTED,
     DLLM_ERR_WORKSPACE,
     DLLM_K_MAX_LIMIT,
+    DLLM_NOALLOC_SCRATCH_BYTES,
     DLLM_OK,
     DLLM_SCORE_CONF,
     DLLM_SCORE_MARGIN,
@@ -35,6 +36,7 @@ from ._abi import (  # noqa: F401
     dllm_masked_readout_step,
     dllm_masked_readout_step_batch,
     dllm_masked_readout_step_ex,
+    dllm_masked_readout_step_noalloc,
     dllm_masked_readout_workspace_bytes,
     dllm_policy,
     dllm_seq,

@@ -20,6 +20,7 @@ DLLM_ERR_WORKSPACE = 3
 DLLM_ERR_HIP = 4
 DLLM_K_MAX_LIMIT = 4096
 DLLM_BATCH_MAX = 128
+DLLM_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 DLLM_SCORE_CONF = 0
 DLLM_SCORE_MARGIN = 1
@@ -36,6 +37,7 @@ EXPORTED = (
     "dllm_status_string",
     "dllm_masked_readout_set_slices",
     "dllm_masked_readout_set_gemm_events",
+    "dllm_masked_readout_step_noalloc",
     "dllm_ffn_workspace_bytes",
     "dllm_ffn_pack_gate_up",
     "dllm_ffn_swiglu_chunked",
@@ -110,6 +112,11 @@ def load(path: str = LIB_PATH):
     lib.dllm_masked_readout_set_slices.argtypes = [C.c_void_p, C.c_int32]
     lib.dllm_masked_readout_set_gemm_events.restype = C.c_int
     lib.dllm_masked_readout_set_gemm_events.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p]
+    lib.dllm_masked_readout_step_noalloc.restype = C.c_int
+    lib.dllm_masked_readout_step_noalloc.argtypes = [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_int64,
+                                                     C.c_void_p, C.c_void_p, C.c_int32, C.c_int64, C.c_int64,
+                                                     C.c_int64, C.POINTER(dllm_policy), C.POINTER(dllm_step_out),
+                                                     C.c_void_p]
     lib.dllm_ffn_workspace_bytes.restype = C.c_size_t
     lib.dllm_ffn_workspace_bytes.argtypes = [C.c_int64, C.c_int64]
     lib.dllm_ffn_pack_gate_up.restype = C.c_int
@@ -188,6 +195,19 @@ def dllm_masked_readout_step_ex(handle, hidden, L: int, mask, tokens, k: int, wi
     return load().dllm_masked_readout_step_ex(handle, _ptr(hidden), L, _ptr(mask), _ptr(tokens), k, win_lo,
                                               win_hi, block, C.byref(policy) if policy is not None else None,
                                               C.byref(so) if so is not None else None)
+
+
+def dllm_masked_readout_step_noalloc(W_lm, V: int, d: int, hidden, L: int, mask, tokens, k: int, win_lo: int,
+                                     win_hi: int, block: int = 0, policy: dllm_policy | None = None,
+                                     out: dict | None = None, stream=None) -> int:
+    """The handle-free step on the library's static device scratch."""
+    so = None
+    if out:
+        so = dllm_step_out(**{key: _ptr(v) for key, v in out.items()})
+    return load().dllm_masked_readout_step_noalloc(_ptr(W_lm), V, d, _ptr(hidden), L, _ptr(mask), _ptr(tokens), k,
+                                                   win_lo, win_hi, block,
+                                                   C.byref(policy) if policy is not None else None,
+                                                   C.byref(so) if so is not None else None, _stream(stream))
 
 
 def dllm_masked_readout_step_batch(handle, B: int, hidden, L: int, mask, tokens, seqs, block: int = 0,

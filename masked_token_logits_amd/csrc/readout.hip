@@ -1,13 +1,20 @@
 // Host side of the readout C ABI: argument checks, workspace carving, choice
 // of the GEMM variant and launch of the step's kernels (compaction, GEMM,
 // merge / selection) on the handle's stream.
-#include "../../include/dllm_readout.h"
+#include "dllm_readout.h"
 #include "readout_internal.h"
 
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <mutex>
 #include <new>
+
+// Scratch of dllm_masked_readout_step_noalloc: one array per GPU, held until
+// the process ends.  In host code `scratch` names a host-side stand-in, not a
+// device address: kernels get the address hipGetSymbolAddress returns for
+// the current device (kept per device in scratch_ptr), never the name.
+static __device__ __align__(256) uint8_t scratch[DLLM_NOALLOC_SCRATCH_BYTES];
 
 struct dllm_readout {
   const uint16_t* W;
@@ -104,6 +111,24 @@ dllm_status ensure_device(dllm_readout* h) {
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     return DLLM_ERR_HIP;
   h->cus = cus;
+  return DLLM_OK;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices];
+
+dllm_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return DLLM_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return DLLM_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DLLM_ERR_HIP;
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
   return DLLM_OK;
 }
 
@@ -331,6 +356,60 @@ dllm_status dllm_masked_readout_step_ex(dllm_readout* h, const uint16_t* hidden,
   a.rows_max = (block > 0 && block < span) ? block : span;
   a.hidden_rows = L;
   return run_step(h, a, pol, o);
+}
+
+dllm_status dllm_masked_readout_step_noalloc(const uint16_t* W_lm, int64_t V, int64_t d, const uint16_t* hidden,
+                                             int64_t L, uint8_t* mask, int32_t* tokens, int32_t k, int64_t win_lo,
+                                             int64_t win_hi, int64_t block, const dllm_policy* policy,
+                                             const dllm_step_out* out, void* stream) {
+  // the checks of create (limits L_max = L, k_max = k) ...
+  if (!W_lm) return DLLM_ERR_INVALID_ARG;
+  if (k > DLLM_K_MAX_LIMIT) return DLLM_ERR_UNSUPPORTED;
+  if (!limits_ok(L, d, V, k)) return DLLM_ERR_INVALID_ARG;
+  if (d % 8 != 0 || !aligned16(W_lm)) return DLLM_ERR_UNSUPPORTED;
+  if (carve(L, V, nullptr, nullptr) > DLLM_NOALLOC_SCRATCH_BYTES) return DLLM_ERR_WORKSPACE;
+  // ... and of the step, all before the first HIP call
+  if (!hidden || !mask || !tokens) return DLLM_ERR_INVALID_ARG;
+  dllm::Policy pol;
+  const dllm_status ps = parse_policy(policy, &pol);
+  if (ps != DLLM_OK) return ps;
+  if (win_lo < 0 || win_lo > win_hi || win_hi > L) return DLLM_ERR_INVALID_ARG;
+  if (block < 0) return DLLM_ERR_INVALID_ARG;
+  if (!aligned16(hidden)) return DLLM_ERR_UNSUPPORTED;
+  void* base = nullptr;
+  const dllm_status ss = scratch_for_current_device(&base);
+  if (ss != DLLM_OK) return ss;
+
+  dllm_readout h;  // host object on the stack: nothing is allocated
+  h.W = W_lm;
+  h.V = V;
+  h.d = d;
+  h.L_max = L;
+  h.k_max = k;
+  h.stream = reinterpret_cast<hipStream_t>(stream);
+  h.cus = 0;
+  h.slices_override = 0;
+  h.log = false;
+  h.ev_before = nullptr;
+  h.ev_after = nullptr;
+  carve(L, V, reinterpret_cast<uint8_t*>(base), &h.ws);
+  dllm_step_out o = {};
+  if (out) o = *out;
+  const int64_t span = win_hi - win_lo;
+  StepArgs a = {};
+  a.hidden = hidden;
+  a.L = L;
+  a.mask = mask;
+  a.tokens = tokens;
+  a.block = block;
+  a.k = k;
+  a.win_lo = win_lo;
+  a.win_hi = win_hi;
+  a.seqs = nullptr;
+  a.B = 1;
+  a.rows_max = (block > 0 && block < span) ? block : span;
+  a.hidden_rows = L;
+  return run_step(&h, a, pol, o);
 }
 
 dllm_status dllm_masked_readout_step_batch(dllm_readout* h, int32_t B, const uint16_t* hidden, int64_t L,

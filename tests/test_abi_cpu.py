@@ -228,3 +228,54 @@ def test_ffn_validation_before_any_hip_call():
     import torch
     if not torch.cuda.is_available():
         assert ffn() == E.DLLM_ERR_HIP
+
+
+def test_step_noalloc_validation_before_any_hip_call():
+    E = mtl
+    W, H, Mk, T = FAKE, FAKE + 0x200000, FAKE + 0x300000, FAKE + 0x400000
+
+    def step(**kw):
+        a = dict(W_lm=W, V=1000, d=64, hidden=H, L=256, mask=Mk, tokens=T, k=4, win_lo=0, win_hi=256, block=0)
+        a.update(kw)
+        return mtl.dllm_masked_readout_step_noalloc(**a)
+
+    assert step(W_lm=None) == E.DLLM_ERR_INVALID_ARG
+    assert step(hidden=None) == E.DLLM_ERR_INVALID_ARG
+    assert step(mask=None) == E.DLLM_ERR_INVALID_ARG
+    assert step(tokens=None) == E.DLLM_ERR_INVALID_ARG
+    assert step(L=0) == E.DLLM_ERR_INVALID_ARG
+    assert step(V=0) == E.DLLM_ERR_INVALID_ARG
+    assert step(k=-1) == E.DLLM_ERR_INVALID_ARG
+    assert step(k=E.DLLM_K_MAX_LIMIT + 1) == E.DLLM_ERR_UNSUPPORTED
+    assert step(d=60) == E.DLLM_ERR_UNSUPPORTED
+    assert step(W_lm=W + 8) == E.DLLM_ERR_UNSUPPORTED
+    assert step(hidden=H + 2) == E.DLLM_ERR_UNSUPPORTED
+    assert step(win_lo=-1) == E.DLLM_ERR_INVALID_ARG
+    assert step(win_lo=10, win_hi=5) == E.DLLM_ERR_INVALID_ARG
+    assert step(win_hi=257) == E.DLLM_ERR_INVALID_ARG
+    assert step(block=-1) == E.DLLM_ERR_INVALID_ARG
+    bad = mtl.dllm_policy(7, 0, 0.0)
+    assert step(policy=bad) == E.DLLM_ERR_INVALID_ARG
+    # sizes whose workspace exceeds the static scratch: rejected, nothing queued
+    big = 200000
+    assert mtl.dllm_masked_readout_workspace_bytes(big, 64, 1000, 4) > E.DLLM_NOALLOC_SCRATCH_BYTES
+    assert step(L=big, win_hi=big) == E.DLLM_ERR_WORKSPACE
+    # the largest L that fits, at the LLaDA-like vocabulary
+    fits = [L for L in (4096, 8192, 16384) if
+            mtl.dllm_masked_readout_workspace_bytes(L, 4096, 126464, 1024) <= E.DLLM_NOALLOC_SCRATCH_BYTES]
+    assert fits == [4096, 8192, 16384]
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(os.path.join(ROOT, "include", "dllm_readout.h")).read()
+    m = re.search(r"#define DLLM_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == _abi.DLLM_NOALLOC_SCRATCH_BYTES
+
+
+def test_step_noalloc_without_device_reports_hip_error():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    r = mtl.dllm_masked_readout_step_noalloc(FAKE, 1000, 64, FAKE + 0x200000, 256, FAKE + 0x300000,
+                                             FAKE + 0x400000, 4, 0, 256, 0)
+    assert r == mtl.DLLM_ERR_HIP
