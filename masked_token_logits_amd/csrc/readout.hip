@@ -6,9 +6,27 @@
 
 #include <stdio.h>
 #include <stdlib.h>
+#include <string.h>
 
 #include <mutex>
 #include <new>
+
+// DLLM_DEBUG builds check the host-side invariants of workspace carving and
+// launch planning (sizes each kernel's grid and indexing rely on) and abort
+// with a message when one fails; release builds compile the checks out.
+#ifdef DLLM_DEBUG
+#define DLLM_DCHECK(cond)                                                                     \
+  do {                                                                                        \
+    if (!(cond)) {                                                                            \
+      fprintf(stderr, "dllm: internal check failed at %s:%d: %s\n", __FILE__, __LINE__, #cond); \
+      abort();                                                                                \
+    }                                                                                         \
+  } while (0)
+#else
+#define DLLM_DCHECK(cond) \
+  do {                    \
+  } while (0)
+#endif
 
 // Scratch of dllm_masked_readout_step_noalloc: one array per GPU, held until
 // the process ends.  In host code `scratch` names a host-side stand-in, not a
@@ -75,6 +93,11 @@ size_t carve(int64_t L_max, int64_t V, uint8_t* base, dllm::Workspace* ws) {
   w.row_entropy = reinterpret_cast<float*>(take(sizeof(float) * (size_t)L_max));
   w.req = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * 4 * (size_t)dllm::kBatchMax));
   w.part_cap = part_cap;
+  DLLM_DCHECK(off % kAlign == 0);
+  DLLM_DCHECK(part_cap >= (L_max + dllm::kLargeBM - 1) / dllm::kLargeBM * dllm::kLargeBM * dllm::kMaxLargeSlices);
+  DLLM_DCHECK(part_cap >= 4 * (int64_t)dllm::kSmallBM * small_slice_count(V));
+  DLLM_DCHECK(!base || (reinterpret_cast<uint8_t*>(w.req) + sizeof(int32_t) * 4 * (size_t)dllm::kBatchMax <=
+                        base + off));
   if (ws) *ws = w;
   return off;
 }
@@ -192,6 +215,11 @@ dllm_status run_step(dllm_readout* h, const StepArgs& a, const dllm::Policy& pol
     plan.fixed_slices = sl;
     plan.tile_rows = dllm::kLargeBM;
   }
+  // every (row, slice) partial of the plan fits the carved partial arrays
+  DLLM_DCHECK(rows_max <= h->L_max && a.hidden_rows <= h->L_max && a.B >= 1 && a.B <= dllm::kBatchMax);
+  DLLM_DCHECK(path != kSmall || 4 * (int64_t)dllm::kSmallBM * plan.fixed_slices <= w.part_cap);
+  DLLM_DCHECK(path != kStreaming || (int64_t)n_rt * dllm::kLargeBM * plan.fixed_slices <= w.part_cap);
+  DLLM_DCHECK(path != kPersistent || (offsets32 && h->d % dllm::kPersistBK == 0 && plan.grid > 0));
   // A single-sequence few-row step has no compaction launch: the GEMM's
   // workgroups find the candidate rows themselves.
   const bool fused = path == kSmall && !batched && rows_max > 0;
@@ -257,7 +285,12 @@ dllm_status run_step(dllm_readout* h, const StepArgs& a, const dllm::Policy& pol
 extern "C" {
 
 const char* dllm_status_string(dllm_status s) {
-  switch (s) {
+  // A C caller may pass any int: read the argument's bits as an int rather
+  // than as the C++ enum, whose valid range ends at the largest enumerator's
+  // bit width (loading 99 as dllm_status is undefined behaviour).
+  int v;
+  memcpy(&v, &s, sizeof v);
+  switch (v) {
     case DLLM_OK: return "ok";
     case DLLM_ERR_INVALID_ARG: return "invalid argument";
     case DLLM_ERR_UNSUPPORTED: return "unsupported argument (shape divisibility, pointer alignment or size limit)";

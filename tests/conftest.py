@@ -9,6 +9,12 @@ if ROOT not in sys.path:
 
 
 def pytest_configure(config):
+    # DLLM_TEST_LIB: run the tests against another build of the library (the
+    # sanitizer test uses it for its host-only ASan/UBSan build)
+    lib = os.environ.get("DLLM_TEST_LIB")
+    if lib:
+        from masked_token_logits_amd import _abi
+        _abi.load(lib)
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: large inputs (full-size configurations)")
 
