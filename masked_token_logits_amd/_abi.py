@@ -86,6 +86,15 @@ def load(path: str = LIB_PATH):
         return _lib
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with `python -m masked_token_logits_amd.build`")
+    # The library must share the process's HIP runtime with PyTorch, which
+    # allocates the buffers: with torch loaded first, the dynamic linker
+    # resolves the library's libamdhip64 to torch's copy.  Loaded the other
+    # way round, the process holds two runtimes and the library's sees no
+    # device.
+    try:
+        import torch  # noqa: F401
+    except ImportError:  # pragma: no cover - the library still loads (host-only uses)
+        pass
     lib = C.CDLL(path)
     lib.dllm_masked_readout_workspace_bytes.restype = C.c_size_t
     lib.dllm_masked_readout_workspace_bytes.argtypes = [C.c_int64, C.c_int64, C.c_int64, C.c_int32]
