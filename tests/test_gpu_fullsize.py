@@ -4,25 +4,34 @@ benchmark times.
 * LLaDA-like semi-AR loop (L=4096, d=4096, V=126464, k=2, blocks of 32, 32
   steps, hidden re-drawn per step): every step is checked against the oracle
   run on the same state, all rows.
-* Dream-like (L=8192, d=3584, V=152064, k=64), long-context low-mask
-  (L=131072, M=13107, k=256) and high-mask (M=117965, k=1024, 5% planted
-  rows): the oracle cannot afford all rows, so it checks sampled rows, every
-  committed row and the rows just below the commit boundary; properties
-  that hold at any size check the rest (the committed set is the top n of
-  the library's own confidences, and no row outside the checked set can
-  reach the boundary within the tolerance).
+* Dream-like (L=8192, d=3584, V=152064, k=64) and long-context low-mask
+  (L=131072, M=13107, k=256): every candidate row against the oracle
+  (token, confidence, log-sum-exp), and the committed set against the
+  oracle's ranking of all rows.  Dream-like also under ranking by negative
+  entropy with a threshold (margin and entropy of every row checked too).
+* Long-context high-mask (M=117965, k=1024, 5% planted rows), top-k by
+  confidence and by margin: every row against the oracle (about three
+  minutes of host time), and, independent of the oracle, every committed
+  row is planted and every planted masked row reads out its planted token.
 * The batched LLaDA-like workload (16 such sequences per step, one pass over
   W_lm): two steps (512 and 480 candidate rows, the persistent GEMM); four
   of the sequences against the oracle on every row, all sixteen by the
   properties that hold at any size.
+
+The oracle runs on chunks of rows spread over a thread pool (one BLAS thread
+per worker); the oracle itself is unchanged.
 """
+import os
+import time
+
 import numpy as np
 import pytest
 
 import oracle
 import workloads as WL
-from _parity import (GAP, REL, check_commit, check_rank_order, check_rows, check_selection, check_self_selection,
-                     run_batch, run_step, to_dev)
+from _parity import (ENTROPY_GAP, MARGIN_GAP, check_commit, check_ext_rows, check_rank_order, check_rows,
+                     check_selection, check_self_selection, run_batch, run_step,
+                     threshold_n_bounds, to_dev)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -61,79 +70,173 @@ def test_llada_semi_ar_32_steps():
     print(f"llada: near-tie rows {total_ties}, band rows {total_band}")
 
 
-def _sampled_case(name, n_random=384, n_boundary=256):
+def _workers() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    share = os.environ.get("OMP_NUM_THREADS", "")
+    if share.isdigit() and int(share) > 0:
+        n = min(n, int(share))
+    return max(1, min(n, 16))
+
+
+def _oracle_rows(H, W, positions, W64, where, chunk=128):
+    """oracle.readout_rows over `positions`, in chunks of rows spread over a
+    thread pool; results in the order of `positions`."""
+    from concurrent.futures import ThreadPoolExecutor, as_completed
+
+    from threadpoolctl import threadpool_limits
+    positions = np.asarray(positions, np.int64)
+    parts = [positions[i:i + chunk] for i in range(0, len(positions), chunk)]
+    res = [None] * len(parts)
+    t0 = time.time()
+    n_w = _workers()
+    with threadpool_limits(limits=1, user_api="blas"), ThreadPoolExecutor(n_w) as ex:
+        futs = {ex.submit(oracle.readout_rows, H, W, p, 2048, W64): i for i, p in enumerate(parts)}
+        done = 0
+        for f in as_completed(futs):
+            res[futs[f]] = f.result()
+            done += 1
+            if done % 16 == 0 or done == len(parts):
+                print(f"[oracle] {where}: {done}/{len(parts)} chunks of {chunk} rows, {time.time() - t0:.0f}s "
+                      f"({n_w} workers)", flush=True)
+    return {key: np.concatenate([r[key] for r in res]) for key in res[0]}
+
+
+def _gpu_step(cfg, Wt, Ht, inp, score="conf", tau=None):
+    """One full-size step on fresh copies of the initial state."""
+    import torch
+    mt = torch.from_numpy(inp.mask).cuda()
+    tt = torch.from_numpy(inp.tokens).cuda()
+    rd = _readout(Wt, cfg.L, cfg.k)
+    g = run_step(rd, Ht, mt, tt, cfg.k, 0, cfg.L, score=score, tau=tau, ext=score != "conf")
+    rd.close()
+    return g
+
+
+def _check_basics(inp, g, cfg):
+    M = int(inp.mask.sum())
+    assert g["M"] == M
+    np.testing.assert_array_equal(g["row_idx"], np.flatnonzero(inp.mask))
+    check_commit(inp.mask, inp.tokens, g)
+
+
+_FULL = {}
+
+
+def _full_case(name):
+    """Inputs, the library's confidence step and the oracle on every row
+    (cached per workload for the tests of this module)."""
+    if name in _FULL:
+        return _FULL[name]
     import torch
     cfg = WL.WORKLOADS[name]
     print(f"[case] full-size {name}: generating", flush=True)
     inp = WL.make(cfg)
-    Wt, Ht, mt, tt = to_dev(inp.W, inp.H, inp.mask, inp.tokens)
-    rd = _readout(Wt, cfg.L, cfg.k)
-    g = run_step(rd, Ht, mt, tt, cfg.k, 0, cfg.L)
-    del Ht
+    Wt, Ht, _, _ = to_dev(inp.W, inp.H, inp.mask, inp.tokens)
+    g = _gpu_step(cfg, Wt, Ht, inp)
+    _check_basics(inp, g, cfg)
+    W64 = oracle.widen_bf16(inp.W)
+    st = _oracle_rows(inp.H, inp.W, g["row_idx"], W64, name)
+    _FULL[name] = (cfg, inp, Wt, Ht, g, st)
+    del W64
+    torch.cuda.synchronize()
+    return _FULL[name]
+
+
+def _every_row_case(name):
+    cfg, inp, Wt, Ht, g, st = _full_case(name)
+    M, n = g["M"], min(cfg.k, g["M"])
+    assert g["n"] == n
+    ties = check_rows(g["row_tok"], g["row_conf"], g["row_lse"], st, name)
+    check_self_selection(g, "conf", cfg.k, None, name)
+    band = check_selection(g["sel_idx"], g["row_idx"], st["logconf"], n, name)
+    check_rank_order(g["sel_idx"], g["row_idx"], st["logconf"], name)
+    print(f"{name}: M={M} n={n} every row checked; near-tie rows={ties} band rows={band}")
+
+
+def test_dream_like_every_row():
+    _every_row_case("dream_like")
+
+
+def test_dream_like_neg_entropy_threshold():
+    """Ranking by negative entropy with a threshold, at full size: margin and
+    entropy of every row, and the threshold count and committed set against
+    the oracle's (same rules as the small policy tests)."""
+    cfg, inp, Wt, Ht, _, st = _full_case("dream_like")
+    so = np.sort(-st["entropy"])[::-1]
+    # a threshold in the widest gap of the oracle's scores between ranks 8
+    # and 40 (the rows' entropies lie within a few 1e-3 nats of each other,
+    # so the gap may be inside the tolerance band: the count is then checked
+    # against the oracle's counts at tau -/+ the band)
+    a, b = 8, 40
+    j = a + int(np.argmax(so[a - 1:b - 1] - so[a:b]))
+    tau = float(0.5 * (so[j - 1] + so[j]))
+    print(f"[case] dream_like neg_entropy tau={tau:.5f} (oracle rows above: {j})", flush=True)
+    g = _gpu_step(cfg, Wt, Ht, inp, score="neg_entropy", tau=tau)
+    _check_basics(inp, g, cfg)
+    check_rows(g["row_tok"], g["row_conf"], g["row_lse"], st, "dream neg_entropy")
+    check_ext_rows(g["row_margin"], g["row_entropy"], st, "dream neg_entropy")
+    n = check_self_selection(g, "neg_entropy", cfg.k, tau, "dream neg_entropy")
+    n_lo, n_hi = threshold_n_bounds(-st["entropy"], tau, cfg.k, ENTROPY_GAP)
+    assert n_lo <= n <= n_hi, (n, n_lo, n_hi, j)
+    assert 1 < n_lo and n_hi < cfg.k, "the threshold, not the clamp, should decide n"
+    check_selection(g["sel_idx"], g["row_idx"], -st["entropy"], n, "dream neg_entropy", gap=ENTROPY_GAP)
+    check_rank_order(g["sel_idx"], g["row_idx"], -st["entropy"], "dream neg_entropy", gap=ENTROPY_GAP)
+    _FULL.pop("dream_like", None)
+
+
+def test_long_context_low_mask_every_row():
+    _every_row_case("long_ctx_low_mask")
+    _FULL.pop("long_ctx_low_mask", None)
+
+
+def test_long_context_high_mask_planted_and_margin():
+    """Top-k by confidence and by margin at full size, every row against the
+    oracle, plus the planted-token checks that need no oracle."""
+    import torch
+    cfg = WL.WORKLOADS["long_ctx_high_mask"]
+    print("[case] full-size long_ctx_high_mask: generating", flush=True)
+    inp = WL.make(cfg)
+    Wt, Ht, _, _ = to_dev(inp.W, inp.H, inp.mask, inp.tokens)
+    g = _gpu_step(cfg, Wt, Ht, inp)
+    gm = _gpu_step(cfg, Wt, Ht, inp, score="margin")
+    del Ht, Wt
     torch.cuda.empty_cache()
-    M = int(inp.mask.sum())
-    n = min(cfg.k, M)
-    assert g["M"] == M and g["n"] == n
-    np.testing.assert_array_equal(g["row_idx"], np.flatnonzero(inp.mask))
-    check_commit(inp.mask, inp.tokens, g)
+    M, n = g["M"], min(cfg.k, g["M"])
+    for r in (g, gm):
+        _check_basics(inp, r, cfg)
+        assert r["n"] == n
+    np.testing.assert_array_equal(gm["row_tok"], g["row_tok"])
+    check_self_selection(g, "conf", cfg.k, None, "lc_high conf")
+    check_self_selection(gm, "margin", cfg.k, None, "lc_high margin")
 
-    # (1) the commit is the library's own top n (confidence desc, position asc), bit-exact
-    keys = np.lexsort((g["row_idx"], -g["row_conf"].astype(np.float64)))
-    np.testing.assert_array_equal(g["sel_idx"], g["row_idx"][keys[:n]])
-    np.testing.assert_array_equal(g["sel_conf"], g["row_conf"][keys[:n]])
-
-    # (2) oracle rows: committed, just below the boundary, and a random sample
-    rng = np.random.default_rng(1000 + cfg.id)
-    if n < M:
-        # every row whose library confidence could, within the tolerances, still
-        # reach the oracle's boundary (with a safety factor), at least n_boundary
-        c_nG = float(g["row_conf"][keys[n - 1]])
-        thr = c_nG * (1 - REL) ** 2 * np.exp(-GAP) * 0.995
-        n_close = int(np.count_nonzero(g["row_conf"][keys[n:]] >= thr))
-        n_boundary = max(n_boundary, n_close + 1)
-    boundary = keys[n:n + n_boundary]
-    sample = rng.choice(M, size=min(n_random, M), replace=False)
-    rows = np.unique(np.concatenate([keys[:n], boundary, sample]))
-    print(f"[case] {name}: oracle on {len(rows)} rows", flush=True)
-    st = oracle.readout_rows(inp.H, inp.W, g["row_idx"][rows])
-    ties = check_rows(g["row_tok"][rows], g["row_conf"][rows], g["row_lse"][rows], st, f"{name}")
-
-    # (3) no unchecked row can reach the oracle's top n: every unchecked row has a
-    # library confidence at or below the last boundary row's, and the sampled
-    # rows bound the library's relative error by REL.
-    if M > n + n_boundary:
-        c_edge = float(g["row_conf"][keys[n + n_boundary - 1]])
-        c_min_sel = float(st["conf"][np.searchsorted(rows, keys[:n])].min())
-        assert c_edge / (1 - REL) < c_min_sel * np.exp(-GAP), \
-            f"{name}: boundary set too small to exclude unchecked rows"
-    band = check_selection(g["sel_idx"], g["row_idx"][rows], st["logconf"], n, f"{name}")
-    check_rank_order(g["sel_idx"], g["row_idx"][rows], st["logconf"], f"{name}")
-    print(f"{name}: M={M} n={n} checked rows={len(rows)} near-tie rows={ties} band rows={band}")
-    return inp, g
-
-
-def test_dream_like_sampled():
-    _sampled_case("dream_like")
-
-
-def test_long_context_low_mask_sampled():
-    _sampled_case("long_ctx_low_mask")
-
-
-def test_long_context_high_mask_planted():
-    inp, g = _sampled_case("long_ctx_high_mask")
+    # independent of the oracle: committed rows are planted rows with their
+    # planted token, and every planted masked row reads out its planted token
     P = inp.plant
     planted = dict(zip(P.rows.tolist(), P.tokens.tolist()))
-    # independent of the oracle: committed rows are planted rows with their planted token
-    for pos, tok in zip(g["sel_idx"], g["sel_tok"]):
-        assert int(pos) in planted, f"committed position {pos} is not planted"
-        assert planted[int(pos)] == int(tok)
-    # every planted masked row reads out its planted token
+    for r in (g, gm):
+        for pos, tok in zip(r["sel_idx"], r["sel_tok"]):
+            assert int(pos) in planted, f"committed position {pos} is not planted"
+            assert planted[int(pos)] == int(tok)
     pos_to_row = {int(p): i for i, p in enumerate(g["row_idx"])}
     masked_planted = [p for p in P.rows.tolist() if inp.mask[p]]
-    got = np.array([g["row_tok"][pos_to_row[p]] for p in masked_planted])
-    want = np.array([planted[p] for p in masked_planted])
-    np.testing.assert_array_equal(got, want)
+    np.testing.assert_array_equal(np.array([g["row_tok"][pos_to_row[p]] for p in masked_planted]),
+                                  np.array([planted[p] for p in masked_planted]))
+
+    W64 = oracle.widen_bf16(inp.W)
+    st = _oracle_rows(inp.H, inp.W, g["row_idx"], W64, "long_ctx_high_mask")
+    del W64
+    ties = check_rows(g["row_tok"], g["row_conf"], g["row_lse"], st, "lc_high")
+    check_rows(gm["row_tok"], gm["row_conf"], gm["row_lse"], st, "lc_high margin step")
+    check_ext_rows(gm["row_margin"], gm["row_entropy"], st, "lc_high margin step")
+    band = check_selection(g["sel_idx"], g["row_idx"], st["logconf"], n, "lc_high conf")
+    check_rank_order(g["sel_idx"], g["row_idx"], st["logconf"], "lc_high conf")
+    band_m = check_selection(gm["sel_idx"], gm["row_idx"], st["margin"], n, "lc_high margin", gap=MARGIN_GAP)
+    check_rank_order(gm["sel_idx"], gm["row_idx"], st["margin"], "lc_high margin", gap=MARGIN_GAP)
+    print(f"long_ctx_high_mask: M={M} n={n} every row checked; near-tie rows={ties} "
+          f"band rows conf={band} margin={band_m}")
 
 
 def test_llada_batch16_two_steps():
