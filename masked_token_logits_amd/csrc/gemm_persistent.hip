@@ -47,6 +47,7 @@
 #include <type_traits>
 
 #include "online_state.h"
+#include "persistent_sched.h"
 
 namespace dllm {
 namespace {
@@ -71,61 +72,6 @@ static_assert(W_DMA_PER_PAIR + DMA_PER_OPERAND == 12 && 2 * DMA_PER_OPERAND + W_
               "the stage waits assume 12 + 4 DMAs per pair of positions");
 static_assert(BM == BN, "square tile assumed by the loader");
 static_assert(BK == 32, "swizzle and DMA layout assume 4 chunks of 16 B per row");
-
-__device__ __forceinline__ int xcd_remap(int bid, int grid) {
-  constexpr int kXcd = 8;
-  const int per = grid / kXcd, rem = grid % kXcd;
-  const int x = bid % kXcd, loc = bid / kXcd;
-  return (x < rem) ? x * (per + 1) + loc : rem * (per + 1) + (x - rem) * per + loc;
-}
-
-// Work-item order.  Items are (row tile, vocabulary slice) pairs, taken in
-// blocks of 32 row tiles x 8 slices; inside a block, sub-blocks of 4 row
-// tiles x 8 slices with the row tile fastest.  With 256 workgroups, a round
-// of the persistent grid is one block, and the 32 workgroups of each XCD
-// (consecutive positions after xcd_remap) hold one 4 x 8 sub-block: in an
-// XCD's L2 every hidden tile is shared by 8 workgroups and every W_lm tile
-// by 4, and all 8 XCDs stream the same 8 W_lm slices at the same time, so
-// each W_lm tile leaves HBM once per 32 row tiles.  Edge blocks shrink; the
-// map is a bijection onto [0, n_rt) x [0, S).
-constexpr int kGroupRows = 32, kGroupSlices = 8, kSubRows = 4;
-
-__device__ __forceinline__ void item_coords(int e, int n_rt, int S, int& rt, int& slice) {
-  const int g = e / (kGroupRows * S);
-  const int e1 = e - g * kGroupRows * S;
-  const int rb = min(kGroupRows, n_rt - g * kGroupRows);
-  const int h = e1 / (rb * kGroupSlices);
-  const int el = e1 - h * rb * kGroupSlices;
-  const int cb = min(kGroupSlices, S - h * kGroupSlices);
-  const int nsub = rb / kSubRows;
-  int r, c;
-  if (el < nsub * kSubRows * cb) {
-    const int sg = el / (kSubRows * cb);
-    const int rem = el - sg * kSubRows * cb;
-    c = rem / kSubRows;
-    r = sg * kSubRows + (rem - c * kSubRows);
-  } else {
-    const int rem = el - nsub * kSubRows * cb;
-    const int rr = rb - nsub * kSubRows;
-    c = rem / rr;
-    r = nsub * kSubRows + (rem - c * rr);
-  }
-  rt = g * kGroupRows + r;
-  slice = h * kGroupSlices + c;
-}
-
-// Wait until at most N of this wave's vector-memory operations are
-// outstanding and all its LDS operations are done, then barrier the
-// workgroup.  The empty asm statements keep the compiler from moving memory
-// accesses across the barrier (s_barrier alone is not a memory fence).
-template <int N>
-__device__ __forceinline__ void stage_sync() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 
 // Round-to-nearest-even float -> bfloat16 bits (finite inputs), two per word.
 __device__ __forceinline__ uint32_t bf16_pack2(float lo, float hi) {
@@ -631,6 +577,423 @@ __device__ __forceinline__ void persistent_items(uint16_t* __restrict__ lds, con
   }
 }
 
+// Whole-line variant of the main loop (d % 64 == 0): 64-deep K stages, both
+// operands streamed by DMAs that read whole 128-byte lines (8 rows x 128 B
+// per wave instruction).  A stage is a hidden tile [256][64] and a W_lm tile
+// [256][64], 32 KiB each, in a ring of NOP = 5 operand slots (160 KiB):
+// operand i (the hidden tile of stage q is 2q, its W_lm tile 2q + 1) lives
+// in slot i % 5.  Whole lines double what one CU can stream from L2 into LDS
+// with four waves (measured 56 against 27.5 B/clk for 64-byte half lines).
+//
+// Stage q, four 16-deep K steps of 16 MFMAs per wave, each K step's MFMAs
+// interleaved with the next K step's fragment loads:
+//   K step 0:    also the DMAs of hidden tile q + 2 (into the slot W_lm tile
+//                q - 1 held);
+//   barrier B(q) after K step 2: this wave's reads of stage q are done
+//                (lgkmcnt(0)) and stage q + 1 has landed (vmcnt(8): only
+//                hidden tile q + 2 may be in flight);
+//   K step 3:    also the DMAs of W_lm tile q + 2 (into the slot hidden tile
+//                q held) and stage q + 1's first fragments.
+// So hidden tiles are queued about two stages before use and W_lm tiles one
+// (the gathered hidden rows miss L2 more often: each XCD's L2 holds four
+// W_lm tiles per hidden tile in flight, and W_lm tiles are shared by all
+// XCDs in the Infinity Cache), and a wave meets one barrier per 64 MFMAs.
+// The prologue queues the hidden and W_lm tiles of stages 0 and 1.
+constexpr int WBK = kPersistWideBK;            // K per stage
+constexpr int OPT = BM * WBK;                  // elements of one operand tile [256][64]
+constexpr int NOP = 5;                         // operand slots
+constexpr int WL_ROWS = 8;                     // rows per whole-line DMA
+constexpr int WL_DMA = BM / WL_ROWS / 4;       // per wave, stage and operand: 8
+static_assert(NOP * OPT * 2 <= 160 * 1024, "LDS budget of the whole-line ring");
+static_assert(WL_DMA == 8, "the stage wait counts 8 DMAs per operand tile and wave");
+
+template <int MODE, bool EXT>
+__device__ __forceinline__ void persistent_items_wl(uint16_t* __restrict__ lds, const uint16_t* __restrict__ W,
+                                                    const uint16_t* __restrict__ H, int d, int V,
+                                                    const int32_t* __restrict__ idx,
+                                                    const int32_t* __restrict__ ctr, Partials part, StoreArgs st) {
+  const int n_vt = (V + BN - 1) / BN;
+  const int M = MODE == kEpiReadout ? ctr[0] : st.M;
+  const int S = MODE == kEpiReadout ? ctr[3] : n_vt;           // store modes: one output tile per item
+  const int n_rt = MODE == kEpiReadout ? ctr[4] : (st.M + BM - 1) / BM;
+  const int n_items = n_rt * S;
+  const int KT = d / WBK;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS DMA addresses stay scalar
+  const int wr = wave >> 1;   // row half: local 32-row blocks wr, wr + 2, wr + 4, wr + 6
+  const int wv = wave & 1;    // vocabulary [wv * 128, +128)
+
+  // LDS layout of a [256][64] bf16 operand tile: row r holds its eight
+  // 16-byte chunks at positions chunk ^ fw(r), fw(r) = (r >> 1) & 7; the 16
+  // rows of a ds_read_b128 phase then fill the 64 banks (even rows one half,
+  // odd rows the other, 8 distinct positions each).  DMA lane geometry: lane
+  // -> row lane / 8 of an 8-row block, LDS position lane % 8, global chunk
+  // position ^ fw(row).
+  const int frag_row = lane & 31;
+  const int frag_half = lane >> 5;
+  const int frag_swz = (frag_row >> 1) & 7;
+
+  for (int e = xcd_remap(blockIdx.x, gridDim.x); e < n_items; e += gridDim.x) {
+    int rt, slice;
+    item_coords(e, n_rt, S, rt, slice);
+    const int row0 = rt * BM;
+    const int nblk = (M + 31) / 32;
+    const int nb = MODE == kEpiReadout ? (rt < nblk ? min(8, (nblk - rt - 1) / n_rt + 1) : 0)
+                                       : min(8, max(0, (M - row0 + 31) / 32));
+    auto grow = [&](int l) {
+      return MODE == kEpiReadout ? ((l >> 5) * n_rt + rt) * 32 + (l & 31) : row0 + l;
+    };
+    const int vt_lo = (int)(((int64_t)slice * n_vt) / S);
+    const int vt_hi = (int)(((int64_t)(slice + 1) * n_vt) / S);
+
+    // DMA j (0..7) of this wave covers rows (wave + 4 j) * 8 + lane / 8 of
+    // a tile; its lane reads global chunk (lane % 8) ^ fw(row).  Hidden rows
+    // as 64-bit byte offsets (any hidden size), rows past M repeat row M - 1;
+    // W_lm rows relative to the tile's first row.
+    uint64_t hoff[WL_DMA];
+    uint32_t woff[WL_DMA];
+#pragma unroll
+    for (int j = 0; j < WL_DMA; ++j) {
+      const int l = (wave + 4 * j) * WL_ROWS + (lane >> 3);
+      const int c = (lane & 7) ^ ((l >> 1) & 7);
+      int r = grow(l);
+      r = r < M ? r : M - 1;
+      const uint64_t src = MODE == kEpiReadout ? (uint64_t)(uint32_t)idx[r] : (uint64_t)r;
+      hoff[j] = (src * (uint64_t)d + (uint64_t)(c * 8)) * 2u;
+      woff[j] = (uint32_t)((l * d + c * 8) * 2);
+    }
+    const char* Hb = reinterpret_cast<const char*>(H);
+
+    // Issue bookkeeping: stage positions are numbered from the item's first
+    // stage; the hidden tile of position q goes to slot (2q) % 5 and its
+    // W_lm tile to (2q + 1) % 5.  Positions past the item's last stage re-read its last
+    // W_lm tile and hidden tile (valid memory) and are never consumed; the
+    // item's final vmcnt(0) drains them.  W_lm rows past V (last vocabulary
+    // tile only) re-read row 0 of the tile; the epilogue drops their logits.
+    int wi_vt = vt_lo, wi_k0 = 0, wi_slot = 1;  // next W_lm position to issue
+    int hi_k0 = 0, hi_slot = 0;                 // next hidden position to issue
+    auto next_slot = [](int s) { return s + 2 >= NOP ? s + 2 - NOP : s + 2; };
+    auto issue_w = [&](int j) {
+      const int vbase = (wi_vt < vt_hi ? wi_vt : vt_hi - 1) * BN;
+      const char* Wb = reinterpret_cast<const char*>(W + (size_t)vbase * (size_t)d + wi_k0);
+      const bool keep = vbase + BN <= V || vbase + (wave + 4 * j) * WL_ROWS + (lane >> 3) < V;
+      const uint32_t o = keep ? woff[j] : (uint32_t)((lane & 7) * 16);
+      __builtin_amdgcn_global_load_lds((const void*)(Wb + o),
+                                       (LDS_AS void*)(lds + wi_slot * OPT + (wave + 4 * j) * WL_ROWS * WBK), 16, 0, 0);
+    };
+    auto advance_w = [&]() {
+      wi_slot = next_slot(wi_slot);
+      wi_k0 += WBK;
+      if (wi_k0 == d) {
+        wi_k0 = 0;
+        ++wi_vt;
+      }
+    };
+    auto issue_h = [&](int j) {
+      const char* Hk = Hb + (size_t)hi_k0 * 2u;
+      __builtin_amdgcn_global_load_lds((const void*)(Hk + hoff[j]),
+                                       (LDS_AS void*)(lds + hi_slot * OPT + (wave + 4 * j) * WL_ROWS * WBK), 16, 0, 0);
+    };
+    auto advance_h = [&]() {
+      hi_slot = next_slot(hi_slot);
+      hi_k0 = hi_k0 + WBK == d ? 0 : hi_k0 + WBK;
+    };
+
+    float run_m[4], run_s[4], run_m2[4], run_t[4];
+    int run_a[4];
+#pragma unroll
+    for (int fr = 0; fr < 4; ++fr) {
+      const RowState e0 = row_state_empty();
+      run_m[fr] = e0.m;
+      run_s[fr] = e0.s;
+      run_m2[fr] = e0.m2;
+      run_t[fr] = e0.t;
+      run_a[fr] = e0.a;
+    }
+    auto get = [&](int fr) {
+      RowState r;
+      r.m = run_m[fr];
+      r.s = run_s[fr];
+      r.m2 = run_m2[fr];
+      r.t = run_t[fr];
+      r.a = run_a[fr];
+      return r;
+    };
+    auto put = [&](int fr, const RowState& r) {
+      run_m[fr] = r.m;
+      run_s[fr] = r.s;
+      run_m2[fr] = r.m2;
+      run_t[fr] = r.t;
+      run_a[fr] = r.a;
+    };
+
+    auto run_tiles = [&](auto nfr_tag) {
+      constexpr int NFR = decltype(nfr_tag)::value;
+      // Fragment i (0..7) of K step kk of the stage in slots (ws, hs): W_lm
+      // block i / 2 when i is even (needed while any block is active), hidden
+      // block i / 2 when odd (if that block is).
+      auto frag = [&](int ws, int hs, int kk, int i, bf16x8* fa, bf16x8* fb) {
+        const int f = i >> 1;
+        const int chunk = ((kk * 2 + frag_half) ^ frag_swz) * 8;
+        if ((i & 1) == 0) {
+          if (NFR > 0)
+            fa[f] = *reinterpret_cast<const bf16x8*>(lds + ws * OPT + (wv * 128 + f * 32 + frag_row) * WBK + chunk);
+        } else {
+          if (f < NFR)
+            fb[f] = *reinterpret_cast<const bf16x8*>(lds + hs * OPT + ((wr + 2 * f) * 32 + frag_row) * WBK + chunk);
+        }
+      };
+
+      // Prologue: operands 0..3 (hidden and W_lm tiles of stages 0 and 1) in
+      // flight; wait for stage 0 (stage 1 may stay: 16 DMAs); stage 0's first
+      // fragments.
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+#pragma unroll
+        for (int j = 0; j < WL_DMA; ++j) issue_h(j);
+        advance_h();
+#pragma unroll
+        for (int j = 0; j < WL_DMA; ++j) issue_w(j);
+        advance_w();
+      }
+      stage_sync<2 * WL_DMA>();
+      bf16x8 fxa[4], fxb[4], fya[4], fyb[4];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) frag(1, 0, 0, i, fxa, fxb);
+
+      f32x16 acc[4][4];
+      const f32x16 zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      int cws = 1, chs = 0;  // stage q's W_lm and hidden slots
+      // 16 MFMAs of one K step from fragments (a, b), in pairs, with
+      // `between(m)` (m = 0..7: the memory work, here fragment m of the next
+      // K step) after pair m.  Fragments load in the order W0, H0, W1, H1,
+      // W2, H2, W3, H3, and the MFMAs run in the matching triangular order
+      // (block (W k, H j) as soon as both are in): pair p of a K step uses
+      // only fragments the previous K step loaded at least five pairs before
+      // its end, so LDS latency never stalls the matrix pipe.  FIRST_K: the
+      // first K step of a vocabulary tile takes an inline zero accumulator
+      // (acc is never explicitly cleared: explicit clears get hoisted above
+      // the epilogue's reads and push the accumulators out of AGPRs).
+      auto kstep = [&](const bf16x8* a, const bf16x8* b, auto first_tag, auto between) {
+        constexpr bool FIRST_K = decltype(first_tag)::value;
+        // (W block, hidden block) of MFMA n
+        constexpr int kOrder[16][2] = {{0, 0}, {1, 0}, {0, 1}, {1, 1}, {2, 0}, {2, 1}, {0, 2}, {1, 2},
+                                       {2, 2}, {3, 0}, {3, 1}, {3, 2}, {0, 3}, {1, 3}, {2, 3}, {3, 3}};
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const int fv = kOrder[2 * m + t][0], fr = kOrder[2 * m + t][1];
+            if (fr < NFR)
+              acc[fv][fr] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[fv], b[fr], FIRST_K ? zero16 : acc[fv][fr],
+                                                                    0, 0, 0);
+          }
+          between(m);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      auto stage = [&](auto first_tag) {
+        const int nws = next_slot(cws), nhs = next_slot(chs);  // stage q + 1's slots
+        kstep(fxa, fxb, first_tag, [&](int m) {
+          issue_h(m);
+          frag(cws, chs, 1, m, fya, fyb);
+        });
+        advance_h();
+        kstep(fya, fyb, std::false_type{}, [&](int m) { frag(cws, chs, 2, m, fxa, fxb); });
+        kstep(fxa, fxb, std::false_type{}, [&](int m) { frag(cws, chs, 3, m, fya, fyb); });
+        // B(q): stage q + 1 landed (only the hidden tile of q + 2 may be in
+        // flight) and every wave is done reading stage q.
+        stage_sync<WL_DMA>();
+        kstep(fya, fyb, std::false_type{}, [&](int m) {
+          issue_w(m);
+          frag(nws, nhs, 0, m, fxa, fxb);
+        });
+        advance_w();
+        cws = nws;
+        chs = nhs;
+      };
+      for (int vt = vt_lo; vt < vt_hi; ++vt) {
+        stage(std::true_type{});
+        for (int ks = 1; ks < KT; ++ks) stage(std::false_type{});
+        if constexpr (NFR > 0) {
+          // Online reduction of the finished vocabulary tile, one 16-value
+          // block at a time.  Accumulator x of block (fv, fr) is vocabulary
+          // entry v0 + fv*32 + 8*(x/4) + x%4 of local row (wr + 2 fr)*32 + lane%32,
+          // with v0 = tile base + wv*128 + 4*(lane/32).  Within a lane the
+          // index grows with (fv, x); strict '>' comparisons in that order
+          // keep the lowest index among equal maxima.
+          // The accumulators are read with explicit v_accvgpr_read (inline
+          // asm): left to itself the register allocator copies all 256 of
+          // them to VGPRs at once and spills.  The compiler does not see these
+          // reads as consumers of the MFMA results for hazard purposes, so 24
+          // wait states are inserted first, ordered after every MFMA by
+          // taking all live accumulators as operands.
+          if constexpr (NFR == 4)
+            asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::"a"(acc[0][0]), "a"(acc[0][1]), "a"(acc[0][2]),
+                         "a"(acc[0][3]), "a"(acc[1][0]), "a"(acc[1][1]), "a"(acc[1][2]), "a"(acc[1][3]),
+                         "a"(acc[2][0]), "a"(acc[2][1]), "a"(acc[2][2]), "a"(acc[2][3]), "a"(acc[3][0]),
+                         "a"(acc[3][1]), "a"(acc[3][2]), "a"(acc[3][3]));
+          else if constexpr (NFR == 3)
+            asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::"a"(acc[0][0]), "a"(acc[0][1]), "a"(acc[0][2]),
+                         "a"(acc[1][0]), "a"(acc[1][1]), "a"(acc[1][2]), "a"(acc[2][0]), "a"(acc[2][1]),
+                         "a"(acc[2][2]), "a"(acc[3][0]), "a"(acc[3][1]), "a"(acc[3][2]));
+          else if constexpr (NFR == 2)
+            asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::"a"(acc[0][0]), "a"(acc[0][1]), "a"(acc[1][0]),
+                         "a"(acc[1][1]), "a"(acc[2][0]), "a"(acc[2][1]), "a"(acc[3][0]), "a"(acc[3][1]));
+          else
+            asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::"a"(acc[0][0]), "a"(acc[1][0]), "a"(acc[2][0]),
+                         "a"(acc[3][0]));
+          if constexpr (MODE == kEpiReadout) {
+            const int v0 = vt * BN + wv * 128 + 4 * frag_half;
+            const bool full = (vt + 1) * BN <= V;
+            auto off = [](int x) { return 8 * (x >> 2) + (x & 3); };
+#pragma unroll
+            for (int fr = 0; fr < NFR; ++fr) {
+#pragma unroll
+              for (int fv = 0; fv < 4; ++fv) {
+                float z[16];
+#pragma unroll
+                for (int x = 0; x < 16; ++x) {
+                  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(z[x]) : "a"(acc[fv][fr][x]));
+                  if (!full && v0 + fv * 32 + off(x) >= V) z[x] = -INFINITY;
+                }
+                RowState r = get(fr);
+                row_fold<EXT, 16>(r, z, v0 + fv * 32, off);
+                put(fr, r);
+              }
+            }
+          } else {
+            // Output tile store (the item's only tile: these stores come after
+            // the last stage's waits, and the item's vmcnt(0) drains them).
+            // Accumulator x of block (fv, fr) is output column
+            // c0 + fv*32 + 8*(x/4) + x%4, c0 = tile base + wv*128 + 4*(lane/32),
+            // of row row0 + (wr + 2 fr)*32 + lane%32: four runs of 4 columns.
+#pragma unroll
+            for (int fr = 0; fr < NFR; ++fr) {
+              const int row = row0 + (wr + 2 * fr) * 32 + frag_row;
+              const bool ok = row < M;
+              uint16_t* orow = st.out + (size_t)(ok ? row : 0) * (size_t)st.ldo;
+              if constexpr (MODE == kEpiStore) {
+                const int c0 = vt * BN + wv * 128 + 4 * frag_half;
+#pragma unroll
+                for (int fv = 0; fv < 4; ++fv) {
+#pragma unroll
+                  for (int j = 0; j < 4; ++j) {
+                    float z[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                      asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(z[i]) : "a"(acc[fv][fr][4 * j + i]));
+                    const uint2 pk = make_uint2(bf16_pack2(z[0], z[1]), bf16_pack2(z[2], z[3]));
+                    if (ok) *reinterpret_cast<uint2*>(orow + c0 + fv * 32 + 8 * j) = pk;
+                  }
+                }
+              } else {
+                // Weight rows come in 64-row units: 32 gate rows, then the 32
+                // up rows of the same outputs.  Blocks (0, 1) and (2, 3) of a
+                // wave are such pairs, so gate and up of one output sit in the
+                // same lane and register position.  Output column
+                // c0 + p*32 + 8*(x/4) + x%4, c0 = tile*128 + wv*64 + 4*(lane/32).
+                const int c0 = vt * (BN / 2) + wv * 64 + 4 * frag_half;
+#pragma unroll
+                for (int pr = 0; pr < 2; ++pr) {
+#pragma unroll
+                  for (int j = 0; j < 4; ++j) {
+                    float a[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                      float g, u;
+                      asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(g) : "a"(acc[2 * pr][fr][4 * j + i]));
+                      asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(u) : "a"(acc[2 * pr + 1][fr][4 * j + i]));
+                      a[i] = swiglu(g, u);
+                    }
+                    const uint2 pk = make_uint2(bf16_pack2(a[0], a[1]), bf16_pack2(a[2], a[3]));
+                    if (ok) *reinterpret_cast<uint2*>(orow + c0 + pr * 32 + 8 * j) = pk;
+                  }
+                }
+              }
+            }
+          }
+        }
+      }
+    };
+    const int nfr = min(4, max(0, (nb - wr + 1) / 2));
+    switch (nfr) {
+      case 4: run_tiles(std::integral_constant<int, 4>{}); break;
+      case 3: run_tiles(std::integral_constant<int, 3>{}); break;
+      case 2: run_tiles(std::integral_constant<int, 2>{}); break;
+      case 1: run_tiles(std::integral_constant<int, 1>{}); break;
+      default: run_tiles(std::integral_constant<int, 0>{}); break;
+    }
+    if constexpr (MODE == kEpiReadout) {
+      // Half-waves hold the same rows with interleaved vocabulary entries.
+  #pragma unroll
+      for (int fr = 0; fr < 4; ++fr) {
+        RowState x = get(fr), y;
+        y.m = __shfl_xor(x.m, 32);
+        y.s = __shfl_xor(x.s, 32);
+        y.m2 = __shfl_xor(x.m2, 32);
+        y.t = __shfl_xor(x.t, 32);
+        y.a = __shfl_xor(x.a, 32);
+        row_merge<EXT>(x, y);
+        put(fr, x);
+      }
+      // The two vocabulary halves (wv = 0, 1) of each row meet in LDS.  All DMAs
+      // have landed (the last stage waited for vmcnt(0)); barrier before reuse.
+      stage_sync<0>();
+      float* xm = reinterpret_cast<float*>(&lds[0]);
+      int* xa = reinterpret_cast<int*>(xm + 2 * BM);
+      float* xs = reinterpret_cast<float*>(xa + 2 * BM);
+      float* xm2 = xs + 2 * BM;
+      float* xt = xm2 + 2 * BM;
+      if (frag_half == 0) {
+  #pragma unroll
+        for (int fr = 0; fr < 4; ++fr) {
+          const int r = (wr + 2 * fr) * 32 + frag_row;
+          xm[wv * BM + r] = run_m[fr];
+          xa[wv * BM + r] = run_a[fr];
+          xs[wv * BM + r] = run_s[fr];
+          if (EXT) {
+            xm2[wv * BM + r] = run_m2[fr];
+            xt[wv * BM + r] = run_t[fr];
+          }
+        }
+      }
+      stage_sync<0>();
+      {
+        const int r = tid;  // NT == BM: one row per thread
+        RowState x, y;
+        x.m = xm[r];
+        x.a = xa[r];
+        x.s = xs[r];
+        x.m2 = EXT ? xm2[r] : -INFINITY;
+        x.t = EXT ? xt[r] : 0.f;
+        y.m = xm[BM + r];
+        y.a = xa[BM + r];
+        y.s = xs[BM + r];
+        y.m2 = EXT ? xm2[BM + r] : -INFINITY;
+        y.t = EXT ? xt[BM + r] : 0.f;
+        row_merge<EXT>(x, y);
+        const int row = grow(r);  // >= M for local blocks past nb
+        if (row < M) {
+          const size_t o = (size_t)row * (size_t)S + (size_t)slice;
+          part.m[o] = x.m;
+          part.a[o] = x.a;
+          part.s[o] = x.s;
+          if (EXT) {
+            part.m2[o] = x.m2;
+            part.t[o] = x.t;
+          }
+        }
+      }
+    }
+    // The next item's prologue overwrites the exchange area and counts vmcnt
+    // from zero: drain the stores and the LDS reads first.
+    stage_sync<0>();
+  }
+}
+
 static_assert(NT == BM, "one thread per row in the final merge");
 
 template <int MODE, bool EXT>
@@ -643,13 +1006,9 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_persistent(const uint16_t* __res
   // vmcnt at every fragment read).
   __shared__ __attribute__((aligned(1024))) uint16_t lds[NWP * WPAIR + NST * TILE];
   static_assert(NST * 2 * TILE <= NWP * WPAIR + NST * TILE, "LDS layouts");
-  if constexpr (MODE == kEpiReadout) {
-    // one row tile: the W_lm stream is the bound; the pairs need an even
-    // stage count per vocabulary tile (uniform over the grid)
-    if (ctr[4] == 1 && (d & (2 * BK - 1)) == 0) {
-      persistent_items<MODE, EXT, true>(lds, W, H, d, V, idx, ctr, part, st);
-      return;
-    }
+  if ((d & (WBK - 1)) == 0) {
+    persistent_items_wl<MODE, EXT>(lds, W, H, d, V, idx, ctr, part, st);
+    return;
   }
   persistent_items<MODE, EXT, false>(lds, W, H, d, V, idx, ctr, part, st);
 }

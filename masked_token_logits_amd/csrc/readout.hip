@@ -127,12 +127,21 @@ dllm_status parse_policy(const dllm_policy* policy, dllm::Policy* pol) {
   return DLLM_OK;
 }
 
+// A failed HIP call of a step: DLLM_ERR_HIP, and with DLLM_LOG=1 the call
+// and HIP's description of the error on stderr.
+dllm_status hip_failed(const dllm_readout* h, const char* what, hipError_t e) {
+  if (h->log) fprintf(stderr, "[dllm] %s failed: %s (%d)\n", what, hipGetErrorString(e), (int)e);
+  return DLLM_ERR_HIP;
+}
+
 dllm_status ensure_device(dllm_readout* h) {
   if (h->cus > 0) return DLLM_OK;
   int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return DLLM_ERR_HIP;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    return DLLM_ERR_HIP;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_failed(h, "hipGetDevice", e);
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_failed(h, "hipDeviceGetAttribute", e);
+  if (cus <= 0) return DLLM_ERR_HIP;
   h->cus = cus;
   return DLLM_OK;
 }
@@ -185,19 +194,23 @@ dllm_status run_step(dllm_readout* h, const StepArgs& a, const dllm::Policy& pol
 
   // Choose the GEMM variant from the host-known bound on M; the slice count
   // of the persistent variant is fixed on the device once M is known.  The
-  // persistent kernel addresses hidden rows and the rows of a W_lm tile with
-  // 32-bit byte offsets, so both must span less than 4 GiB.
+  // persistent kernel addresses the rows of a W_lm tile with 32-bit byte
+  // offsets (256 rows x d < 4 GiB).  Hidden rows: 64-bit offsets in its
+  // whole-line main loop (d % 64 == 0), 32-bit in the half-line one
+  // (d % 64 == 32), which therefore needs a hidden tensor under 4 GiB.
   enum { kSmall, kPersistent, kStreaming } path;
   const int64_t n_vt_large = (h->V + dllm::kLargeBN - 1) / dllm::kLargeBN;
-  const bool offsets32 = a.hidden_rows * h->d * 2 < ((int64_t)1 << 32) &&
-                         (int64_t)dllm::kPersistBN * h->d * 2 < ((int64_t)1 << 32);
+  const bool w_tile32 = (int64_t)dllm::kPersistBN * h->d * 2 < ((int64_t)1 << 32);
+  const bool hidden32 = a.hidden_rows * h->d * 2 < ((int64_t)1 << 32);
+  const bool persistent_ok =
+      h->d % dllm::kPersistBK == 0 && w_tile32 && (h->d % dllm::kPersistWideBK == 0 || hidden32);
   dllm::PlanParams plan = {};
   int n_rt = 0;
   if (rows_max <= dllm::kSmallBM) {
     path = kSmall;
     plan.fixed_slices = (int)small_slice_count(h->V);
     plan.tile_rows = dllm::kSmallBM;
-  } else if (h->d % dllm::kPersistBK == 0 && offsets32) {
+  } else if (persistent_ok) {
     path = kPersistent;
     int so = h->slices_override;
     if (so > n_vt_large) so = (int)n_vt_large;
@@ -219,7 +232,7 @@ dllm_status run_step(dllm_readout* h, const StepArgs& a, const dllm::Policy& pol
   DLLM_DCHECK(rows_max <= h->L_max && a.hidden_rows <= h->L_max && a.B >= 1 && a.B <= dllm::kBatchMax);
   DLLM_DCHECK(path != kSmall || 4 * (int64_t)dllm::kSmallBM * plan.fixed_slices <= w.part_cap);
   DLLM_DCHECK(path != kStreaming || (int64_t)n_rt * dllm::kLargeBM * plan.fixed_slices <= w.part_cap);
-  DLLM_DCHECK(path != kPersistent || (offsets32 && h->d % dllm::kPersistBK == 0 && plan.grid > 0));
+  DLLM_DCHECK(path != kPersistent || (persistent_ok && plan.grid > 0));
   // A single-sequence few-row step has no compaction launch: the GEMM's
   // workgroups find the candidate rows themselves.
   const bool fused = path == kSmall && !batched && rows_max > 0;
@@ -230,13 +243,16 @@ dllm_status run_step(dllm_readout* h, const StepArgs& a, const dllm::Policy& pol
     ce = dllm::launch_mask_compact_small(a.mask, a.win_lo, a.win_hi, a.block, plan.fixed_slices, w.idx, w.ctr, st);
   else if (path != kSmall)
     ce = dllm::launch_mask_compact(a.mask, a.win_lo, a.win_hi, a.block, plan, w.idx, w.ctr, st);
-  if (ce != hipSuccess) return DLLM_ERR_HIP;
+  if (ce != hipSuccess) return hip_failed(h, "compaction launch", ce);
 
   const int32_t* req = batched ? w.req : nullptr;
   const int k_stride = h->k_max;
   if (rows_max > 0) {
     hipError_t e;
-    if (h->ev_before && hipEventRecord(h->ev_before, st) != hipSuccess) return DLLM_ERR_HIP;
+    if (h->ev_before) {
+      const hipError_t er = hipEventRecord(h->ev_before, st);
+      if (er != hipSuccess) return hip_failed(h, "hipEventRecord", er);
+    }
     if (path == kSmall) {
       const dllm::FindRows fr = {a.mask, a.win_lo, a.win_hi, a.block, w.idx, w.ctr};
       e = dllm::launch_gemm_small(h->W, a.hidden, d, V, w.idx, w.ctr, plan.fixed_slices, parts,
@@ -252,14 +268,17 @@ dllm_status run_step(dllm_readout* h, const StepArgs& a, const dllm::Policy& pol
               fused ? "small-find" : path == kSmall ? "small" : path == kPersistent ? "persistent" : "streaming",
               plan.fixed_slices, h->cus,
               (int)ext, pol.score, pol.use_threshold);
-    if (e != hipSuccess) return DLLM_ERR_HIP;
-    if (h->ev_after && hipEventRecord(h->ev_after, st) != hipSuccess) return DLLM_ERR_HIP;
+    if (e != hipSuccess) return hip_failed(h, "GEMM launch", e);
+    if (h->ev_after) {
+      const hipError_t er = hipEventRecord(h->ev_after, st);
+      if (er != hipSuccess) return hip_failed(h, "hipEventRecord", er);
+    }
     if (path == kSmall) {
       // merge (one workgroup per row), selection and commit of <= 32 rows
       const dllm::FewRowResults res = {w.row_tok, w.row_conf, w.row_lse, w.row_margin, w.row_entropy};
-      if (dllm::launch_finish_small(w.ctr, w.idx, req, a.B, a.L, k_stride, parts, pol, a.k, a.mask, a.tokens, o,
-                                    res, st) != hipSuccess)
-        return DLLM_ERR_HIP;
+      const hipError_t ef = dllm::launch_finish_small(w.ctr, w.idx, req, a.B, a.L, k_stride, parts, pol, a.k, a.mask,
+                                                      a.tokens, o, res, st);
+      if (ef != hipSuccess) return hip_failed(h, "few-row finish launch", ef);
       return DLLM_OK;
     }
     // single sequence: the merge writes the row outputs; batched: it fills
@@ -271,12 +290,12 @@ dllm_status run_step(dllm_readout* h, const StepArgs& a, const dllm::Policy& pol
     } else {
       om = o;
     }
-    if (dllm::launch_merge(w.ctr, w.idx, parts, pol.score, (int)rows_max, w.row_tok, w.row_conf, w.row_lse,
-                           w.keys, om, st) != hipSuccess)
-      return DLLM_ERR_HIP;
+    const hipError_t em = dllm::launch_merge(w.ctr, w.idx, parts, pol.score, (int)rows_max, w.row_tok, w.row_conf,
+                                             w.row_lse, w.keys, om, st);
+    if (em != hipSuccess) return hip_failed(h, "merge launch", em);
   }
-  if (dllm::launch_topk_scatter(w.ctr, req, a.B, a.L, k_stride, a.k, pol, w, a.mask, a.tokens, o, st) != hipSuccess)
-    return DLLM_ERR_HIP;
+  const hipError_t es = dllm::launch_topk_scatter(w.ctr, req, a.B, a.L, k_stride, a.k, pol, w, a.mask, a.tokens, o, st);
+  if (es != hipSuccess) return hip_failed(h, "selection launch", es);
   return DLLM_OK;
 }
 

@@ -96,8 +96,11 @@ hipError_t launch_gemm_large(const uint16_t* W, const uint16_t* H, int d, int V,
                              const int32_t* ctr, int n_row_tiles, int slices, Partials p, hipStream_t stream);
 
 // Persistent compute-bound variant (d % 32 == 0): `grid` workgroups walk the
-// (row tile, slice) items of the device-side plan in ctr[3], ctr[4].
+// (row tile, slice) items of the device-side plan in ctr[3], ctr[4].  With
+// d % kPersistWideBK == 0 its main loop runs 64-deep stages of whole
+// 128-byte lines; otherwise 32-deep stages of half lines.
 constexpr int kPersistBM = 256, kPersistBN = 256, kPersistBK = 32, kPersistStages = 4;
+constexpr int kPersistWideBK = 64;
 hipError_t launch_gemm_persistent(const uint16_t* W, const uint16_t* H, int d, int V, const int32_t* idx,
                                   const int32_t* ctr, int grid, Partials p, hipStream_t stream);
 

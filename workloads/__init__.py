@@ -165,6 +165,12 @@ def _normal_bf16(n_rows: int, n_cols: int, std: float, config_id: int, stream: i
     return out
 
 
+def random_rows(n_rows: int, n_cols: int, std: float, config_id: int, stream: int) -> np.ndarray:
+    """[n_rows, n_cols] bf16 bits of seeded N(0, std) draws (tests that place a
+    few rows inside a large, otherwise unread tensor)."""
+    return _normal_bf16(n_rows, n_cols, std, config_id, stream)
+
+
 def w_lm(cfg: Config) -> np.ndarray:
     """LM head W_lm [V, d], bf16 bits, N(0, 0.02)."""
     return _normal_bf16(cfg.V, cfg.d, W_STD, cfg.id, STREAM_W)
