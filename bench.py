@@ -106,11 +106,14 @@ def cpu_share() -> tuple[int, int]:
     return max(1, n), visible
 
 
+KERNEL_HEADERS = ("readout_internal.h", "online_state.h", "few_rows.h", "persistent_sched.h")
+
+
 def kernel_source_sha(kernel_src: str) -> str:
-    """sha256 over a GEMM kernel's source and the headers its code comes from."""
+    """sha256 over a GEMM kernel's source and the headers its code comes from
+    (KERNEL_HEADERS, in that order, after the source)."""
     h = hashlib.sha256()
-    for f in (kernel_src, os.path.join(CSRC, "readout_internal.h"), os.path.join(CSRC, "online_state.h"),
-              os.path.join(CSRC, "few_rows.h")):
+    for f in (kernel_src,) + tuple(os.path.join(CSRC, x) for x in KERNEL_HEADERS):
         h.update(open(f, "rb").read())
     return h.hexdigest()
 
@@ -577,6 +580,45 @@ def bench_readout(args, short: str) -> dict:
     return rec
 
 
+def gemm_ceiling(stages: int = 20000, reps: int = 5) -> dict:
+    """The compute-bound GEMM's practical ceiling on this GPU: its main
+    loop's instruction mix alone (dllm_probe_gemm_mix) on random bf16
+    operands, one workgroup per compute unit; median of `reps` launches."""
+    import torch
+
+    import masked_token_logits_amd as mtl
+    dev = torch.device("cuda", 0)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    g = torch.Generator(device=dev)
+    g.manual_seed(0xD11A)
+    n = mtl.dllm_probe_source_bytes() // 2
+    src = torch.randn(n, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    sink = torch.empty(cus * 256, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    out = {"grid": cus, "stages": stages, "reps": reps,
+           "how": "one 256-thread workgroup per CU; mode 0 = 64 v_mfma_f32_32x32x16_bf16 per wave and stage on "
+                  "fragments held in registers; mode 1 = the main loop's mix (64 MFMAs, 32 ds_read_b128, 16 "
+                  "whole-line global_load_lds from an L2-resident region, one barrier per stage); operands are "
+                  "N(0,1) bf16 values, whose bit toggling sets the sustained MFMA clock"}
+    flops = float(cus) * 4 * stages * 64 * 32768.0
+    for mode, key in ((0, "mfma_only"), (1, "main_loop_mix")):
+        times = []
+        for r in range(reps + 1):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            st = mtl.dllm_probe_gemm_mix(mode, src, stages if r else 100, sink, cus, stream)
+            b.record(stream)
+            if st != mtl.DLLM_OK:
+                raise mtl.DllmError(st, "dllm_probe_gemm_mix")
+            torch.cuda.synchronize()
+            if r:
+                times.append(a.elapsed_time(b))
+        ms = sorted(times)[len(times) // 2]
+        tf = flops / (ms * 1e-3) / 1e12
+        out[key] = {"tflops": round(tf, 1), "frac_of_peak": round(tf / BF16_PEAK_TFLOPS, 4), "ms": round(ms, 3)}
+    return out
+
+
 # The five seeded workloads of the default run, in order; the last is the headline.
 ALL_ORDER = ("tiny", "llada", "dream", "lc_low", "lc_high")
 NESTED_DROP = ("metric", "n_gpus", "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "steps", "warmup")
@@ -596,6 +638,8 @@ def main(argv=None) -> int:
                     help="ranking score of the selection (default: confidence)")
     ap.add_argument("--tau", type=float, default=None,
                     help="threshold commits (score >= tau, at least 1, at most k) instead of top-k")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="only measure the compute-bound GEMM's instruction-mix ceiling (dllm_probe_gemm_mix)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 3 times (reference for HBM byte counters)")
     args = ap.parse_args(argv)
@@ -626,6 +670,9 @@ def main(argv=None) -> int:
         print(json.dumps({"copy_calibration_bytes": 1 << 30, "copies": 3}))
         return 0
     mtl.load()
+    if args.ceiling:
+        print(json.dumps({"gemm_ceiling": gemm_ceiling()}), flush=True)
+        return 0
     if args.workload in FFN_WORKLOADS:
         rec = bench_ffn(args, FFN_WORKLOADS[args.workload])
     elif args.workload != "all":
@@ -645,6 +692,11 @@ def main(argv=None) -> int:
         rec["config"] = dict(rec["config"])
         rec["config"]["headline"] = ("the largest single-GPU workload, MFMA-bound; the other four are nested "
                                      "under 'configs' with their own roofline, latency, memory and CPU baseline")
+        log("[bench] measuring the GEMM's instruction-mix ceiling")
+        ceil = gemm_ceiling()
+        rec["roofline"] = dict(rec["roofline"])
+        rec["roofline"]["gemm_ceiling"] = ceil
+        rec["roofline"]["frac_of_ceiling"] = round(rec["roofline"]["achieved"] / ceil["main_loop_mix"]["tflops"], 4)
     print(json.dumps(rec), flush=True)
     return 0
 

@@ -38,6 +38,8 @@ from ._abi import (  # noqa: F401
     dllm_masked_readout_step_ex,
     dllm_masked_readout_step_noalloc,
     dllm_masked_readout_workspace_bytes,
+    dllm_probe_gemm_mix,
+    dllm_probe_source_bytes,
     dllm_policy,
     dllm_seq,
     dllm_status_string,

@@ -41,6 +41,8 @@ EXPORTED = (
     "dllm_ffn_workspace_bytes",
     "dllm_ffn_pack_gate_up",
     "dllm_ffn_swiglu_chunked",
+    "dllm_probe_source_bytes",
+    "dllm_probe_gemm_mix",
 )
 
 
@@ -126,6 +128,10 @@ def load(path: str = LIB_PATH):
                                                      C.c_void_p, C.c_void_p, C.c_int32, C.c_int64, C.c_int64,
                                                      C.c_int64, C.POINTER(dllm_policy), C.POINTER(dllm_step_out),
                                                      C.c_void_p]
+    lib.dllm_probe_source_bytes.restype = C.c_size_t
+    lib.dllm_probe_source_bytes.argtypes = []
+    lib.dllm_probe_gemm_mix.restype = C.c_int
+    lib.dllm_probe_gemm_mix.argtypes = [C.c_int32, C.c_void_p, C.c_int32, C.c_void_p, C.c_int32, C.c_void_p]
     lib.dllm_ffn_workspace_bytes.restype = C.c_size_t
     lib.dllm_ffn_workspace_bytes.argtypes = [C.c_int64, C.c_int64]
     lib.dllm_ffn_pack_gate_up.restype = C.c_int
@@ -217,6 +223,14 @@ def dllm_masked_readout_step_noalloc(W_lm, V: int, d: int, hidden, L: int, mask,
                                                    win_lo, win_hi, block,
                                                    C.byref(policy) if policy is not None else None,
                                                    C.byref(so) if so is not None else None, _stream(stream))
+
+
+def dllm_probe_source_bytes() -> int:
+    return int(load().dllm_probe_source_bytes())
+
+
+def dllm_probe_gemm_mix(mode: int, src, stages: int, sink, grid: int, stream=None) -> int:
+    return load().dllm_probe_gemm_mix(int(mode), _ptr(src), int(stages), _ptr(sink), int(grid), _stream(stream))
 
 
 def dllm_masked_readout_step_batch(handle, B: int, hidden, L: int, mask, tokens, seqs, block: int = 0,

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libdllm_readout.so")
 SOURCES = ["readout.hip", "mask_compact.hip", "gemm_online.hip", "gemm_persistent.hip", "merge_select.hip",
-           "ffn.hip"]
+           "ffn.hip", "probe.hip"]
 ARCH = "gfx950"
 
 

@@ -279,3 +279,15 @@ def test_step_noalloc_without_device_reports_hip_error():
     r = mtl.dllm_masked_readout_step_noalloc(FAKE, 1000, 64, FAKE + 0x200000, 256, FAKE + 0x300000,
                                              FAKE + 0x400000, 4, 0, 256, 0)
     assert r == mtl.DLLM_ERR_HIP
+
+
+def test_probe_validation_before_any_hip_call():
+    E = mtl
+    assert mtl.dllm_probe_source_bytes() == 32 << 20
+    S, K = FAKE, FAKE + 0x4000000
+    assert mtl.dllm_probe_gemm_mix(2, S, 10, K, 256) == E.DLLM_ERR_INVALID_ARG
+    assert mtl.dllm_probe_gemm_mix(0, None, 10, K, 256) == E.DLLM_ERR_INVALID_ARG
+    assert mtl.dllm_probe_gemm_mix(0, S, 0, K, 256) == E.DLLM_ERR_INVALID_ARG
+    assert mtl.dllm_probe_gemm_mix(1, S, 10, None, 256) == E.DLLM_ERR_INVALID_ARG
+    assert mtl.dllm_probe_gemm_mix(1, S, 10, K, 0) == E.DLLM_ERR_INVALID_ARG
+    assert mtl.dllm_probe_gemm_mix(1, S + 2, 10, K, 256) == E.DLLM_ERR_UNSUPPORTED

@@ -62,3 +62,17 @@ def test_bench_default_line_nests_workloads(capsys, monkeypatch):
     nested = rec["configs"]["tiny"]
     assert "metric" not in nested and nested["value"] > 0
     _check_record(dict(nested, unit="masked tokens/s"), 4)
+
+
+def test_bench_gemm_ceiling(capsys):
+    """The GEMM instruction-mix probe runs and gives plausible rates: both
+    below the published dense peak, the full mix no faster than MFMAs alone
+    (within run-to-run noise)."""
+    import bench
+    print("[case] bench.py --ceiling", flush=True)
+    assert bench.main(["--ceiling"]) == 0
+    rec = _line(capsys)["gemm_ceiling"]
+    a, b = rec["mfma_only"], rec["main_loop_mix"]
+    assert 0 < b["tflops"] <= a["tflops"] * 1.1
+    assert a["frac_of_peak"] < 1.0 and b["frac_of_peak"] < 1.0
+    assert rec["grid"] > 0 and rec["stages"] > 0
