@@ -594,6 +594,7 @@ def gemm_ceiling(stages: int = 20000, reps: int = 5) -> dict:
     n = mtl.dllm_probe_source_bytes() // 2
     src = torch.randn(n, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
     sink = torch.empty(cus * 256, dtype=torch.float32, device=dev)
+    clocks = torch.zeros(2, dtype=torch.int64, device=dev)
     stream = torch.cuda.current_stream(dev)
     out = {"grid": cus, "stages": stages, "reps": reps,
            "how": "one 256-thread workgroup per CU; mode 0 = 64 v_mfma_f32_32x32x16_bf16 per wave and stage on "
@@ -606,7 +607,7 @@ def gemm_ceiling(stages: int = 20000, reps: int = 5) -> dict:
         for r in range(reps + 1):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
-            st = mtl.dllm_probe_gemm_mix(mode, src, stages if r else 100, sink, cus, stream)
+            st = mtl.dllm_probe_gemm_mix(mode, src, stages if r else 100, sink, cus, clocks, stream)
             b.record(stream)
             if st != mtl.DLLM_OK:
                 raise mtl.DllmError(st, "dllm_probe_gemm_mix")
@@ -616,6 +617,13 @@ def gemm_ceiling(stages: int = 20000, reps: int = 5) -> dict:
         ms = sorted(times)[len(times) // 2]
         tf = flops / (ms * 1e-3) / 1e12
         out[key] = {"tflops": round(tf, 1), "frac_of_peak": round(tf / BF16_PEAK_TFLOPS, 4), "ms": round(ms, 3)}
+        cyc, ticks = (int(x) for x in clocks.cpu().tolist())
+        khz = mtl.dllm_probe_wall_clock_khz()
+        if ticks > 0 and khz > 0:
+            ghz = cyc / (ticks / (khz * 1e3)) / 1e9
+            out[key]["shader_clock_ghz"] = round(ghz, 3)
+            # MFMA pipe busy fraction at that clock: 32 cycles per 32x32x16 MFMA
+            out[key]["mfma_busy_at_clock"] = round(tf * 1e12 / (cus * 4 * 1024.0 * ghz * 1e9), 4)
     return out
 
 

@@ -32,6 +32,10 @@ extern "C" {
 /* Bytes of the operand source buffer the probe reads (32 MiB). */
 size_t dllm_probe_source_bytes(void);
 
+/* Rate of the current device's constant wall clock in kHz (the unit of the
+ * second `clocks` value below); 0 if there is no device. */
+int64_t dllm_probe_wall_clock_khz(void);
+
 /*
  * Queue one probe kernel on `stream` (NULL = default stream); returns
  * without waiting.
@@ -41,12 +45,17 @@ size_t dllm_probe_source_bytes(void);
  *   stages  64-deep K stages per workgroup (>= 1)
  *   sink    device float [grid * 256], written (keeps the work live)
  *   grid    workgroups: the compute-unit count for one per CU
+ *   clocks  optional device uint64 [2] (NULL = not wanted): the shader-clock
+ *           cycles (s_memtime) and the constant-rate wall-clock ticks
+ *           (s_memrealtime, hipDeviceAttributeWallClockRate kHz) that wave 0
+ *           of workgroup 0 spent in the loop; their ratio is the sustained
+ *           shader clock under this load
  * DLLM_ERR_INVALID_ARG for a null pointer, stages < 1, grid < 1 or another
  * mode; DLLM_ERR_UNSUPPORTED for a misaligned src; DLLM_ERR_HIP if the
  * launch fails.
  */
 dllm_status dllm_probe_gemm_mix(int32_t mode, const uint16_t *src, int32_t stages, float *sink, int32_t grid,
-                                void *stream);
+                                uint64_t *clocks, void *stream);
 
 #ifdef __cplusplus
 }

@@ -40,6 +40,7 @@ from ._abi import (  # noqa: F401
     dllm_masked_readout_workspace_bytes,
     dllm_probe_gemm_mix,
     dllm_probe_source_bytes,
+    dllm_probe_wall_clock_khz,
     dllm_policy,
     dllm_seq,
     dllm_status_string,

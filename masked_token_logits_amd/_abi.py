@@ -42,6 +42,7 @@ EXPORTED = (
     "dllm_ffn_pack_gate_up",
     "dllm_ffn_swiglu_chunked",
     "dllm_probe_source_bytes",
+    "dllm_probe_wall_clock_khz",
     "dllm_probe_gemm_mix",
 )
 
@@ -130,8 +131,11 @@ def load(path: str = LIB_PATH):
                                                      C.c_void_p]
     lib.dllm_probe_source_bytes.restype = C.c_size_t
     lib.dllm_probe_source_bytes.argtypes = []
+    lib.dllm_probe_wall_clock_khz.restype = C.c_int64
+    lib.dllm_probe_wall_clock_khz.argtypes = []
     lib.dllm_probe_gemm_mix.restype = C.c_int
-    lib.dllm_probe_gemm_mix.argtypes = [C.c_int32, C.c_void_p, C.c_int32, C.c_void_p, C.c_int32, C.c_void_p]
+    lib.dllm_probe_gemm_mix.argtypes = [C.c_int32, C.c_void_p, C.c_int32, C.c_void_p, C.c_int32, C.c_void_p,
+                                        C.c_void_p]
     lib.dllm_ffn_workspace_bytes.restype = C.c_size_t
     lib.dllm_ffn_workspace_bytes.argtypes = [C.c_int64, C.c_int64]
     lib.dllm_ffn_pack_gate_up.restype = C.c_int
@@ -229,8 +233,13 @@ def dllm_probe_source_bytes() -> int:
     return int(load().dllm_probe_source_bytes())
 
 
-def dllm_probe_gemm_mix(mode: int, src, stages: int, sink, grid: int, stream=None) -> int:
-    return load().dllm_probe_gemm_mix(int(mode), _ptr(src), int(stages), _ptr(sink), int(grid), _stream(stream))
+def dllm_probe_wall_clock_khz() -> int:
+    return int(load().dllm_probe_wall_clock_khz())
+
+
+def dllm_probe_gemm_mix(mode: int, src, stages: int, sink, grid: int, clocks=None, stream=None) -> int:
+    return load().dllm_probe_gemm_mix(int(mode), _ptr(src), int(stages), _ptr(sink), int(grid), _ptr(clocks),
+                                      _stream(stream))
 
 
 def dllm_masked_readout_step_batch(handle, B: int, hidden, L: int, mask, tokens, seqs, block: int = 0,

@@ -28,7 +28,7 @@ constexpr int kSlots = 5, kSlotElems = 256 * 64;
 
 template <int MODE>
 __global__ __launch_bounds__(256, 1) void k_probe(const uint16_t* __restrict__ src, int stages,
-                                                   float* __restrict__ sink) {
+                                                   float* __restrict__ sink, uint64_t* __restrict__ clocks) {
   __shared__ __attribute__((aligned(1024))) uint16_t lds[kSlots * kSlotElems];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -92,6 +92,12 @@ __global__ __launch_bounds__(256, 1) void k_probe(const uint16_t* __restrict__ s
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_s_barrier();
   }
+  // shader clock and constant-rate wall clock around the loop (workgroup 0, wave 0)
+  uint64_t c0 = 0, w0 = 0;
+  if (clocks && blockIdx.x == 0 && threadIdx.x == 0) {
+    c0 = clock64();
+    w0 = wall_clock64();
+  }
   for (int q = 0; q < stages; ++q) {
     kstep(0, 1, true);
     kstep(1, 2, false);
@@ -107,6 +113,10 @@ __global__ __launch_bounds__(256, 1) void k_probe(const uint16_t* __restrict__ s
     slot = slot == kSlots - 1 ? 0 : slot + 1;
   }
   __builtin_amdgcn_s_waitcnt(0);
+  if (clocks && blockIdx.x == 0 && threadIdx.x == 0) {
+    clocks[0] = clock64() - c0;
+    clocks[1] = wall_clock64() - w0;
+  }
   float s = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -121,15 +131,22 @@ extern "C" {
 
 size_t dllm_probe_source_bytes(void) { return (size_t)8 * kRegionRows * kRowBytes; }
 
+int64_t dllm_probe_wall_clock_khz(void) {
+  int dev = 0, khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess) return 0;
+  return khz;
+}
+
 dllm_status dllm_probe_gemm_mix(int32_t mode, const uint16_t* src, int32_t stages, float* sink, int32_t grid,
-                                void* stream) {
+                                uint64_t* clocks, void* stream) {
   if (!src || !sink || stages < 1 || grid < 1 || (mode != 0 && mode != 1)) return DLLM_ERR_INVALID_ARG;
   if (((uintptr_t)src & 15u) != 0) return DLLM_ERR_UNSUPPORTED;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (mode == 0)
-    hipLaunchKernelGGL(k_probe<0>, dim3(grid), dim3(256), 0, st, src, stages, sink);
+    hipLaunchKernelGGL(k_probe<0>, dim3(grid), dim3(256), 0, st, src, stages, sink, clocks);
   else
-    hipLaunchKernelGGL(k_probe<1>, dim3(grid), dim3(256), 0, st, src, stages, sink);
+    hipLaunchKernelGGL(k_probe<1>, dim3(grid), dim3(256), 0, st, src, stages, sink, clocks);
   return hipGetLastError() == hipSuccess ? DLLM_OK : DLLM_ERR_HIP;
 }
 

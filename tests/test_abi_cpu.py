@@ -291,3 +291,10 @@ def test_probe_validation_before_any_hip_call():
     assert mtl.dllm_probe_gemm_mix(1, S, 10, None, 256) == E.DLLM_ERR_INVALID_ARG
     assert mtl.dllm_probe_gemm_mix(1, S, 10, K, 0) == E.DLLM_ERR_INVALID_ARG
     assert mtl.dllm_probe_gemm_mix(1, S + 2, 10, K, 256) == E.DLLM_ERR_UNSUPPORTED
+
+
+def test_probe_wall_clock_without_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    assert mtl.dllm_probe_wall_clock_khz() == 0

@@ -76,3 +76,7 @@ def test_bench_gemm_ceiling(capsys):
     assert 0 < b["tflops"] <= a["tflops"] * 1.1
     assert a["frac_of_peak"] < 1.0 and b["frac_of_peak"] < 1.0
     assert rec["grid"] > 0 and rec["stages"] > 0
+    # the sustained shader clock under MFMA load, and the pipe busy fraction at it
+    for r in (a, b):
+        assert 0.5 < r["shader_clock_ghz"] < 3.0
+        assert 0 < r["mfma_busy_at_clock"] <= 1.05

@@ -13,8 +13,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "masked_token_logits_amd", "csrc")
-SOURCES = ["readout.hip", "mask_compact.hip", "gemm_online.hip", "gemm_persistent.hip", "merge_select.hip",
-           "ffn.hip"]
+sys.path.insert(0, ROOT)
+from masked_token_logits_amd.build import SOURCES  # noqa: E402  (the library's own source list)
 
 
 def _asan_runtime(hipcc):
