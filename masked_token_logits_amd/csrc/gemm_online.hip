@@ -237,9 +237,15 @@ __global__ __launch_bounds__(T::NT, T::MIN_WAVES) void k_gemm_online(const uint1
       for (int fr = 0; fr < T::FR; ++fr) {
         float z[T::FV * 16];
 #pragma unroll
-        for (int i = 0; i < T::FV * 16; ++i) {
-          z[i] = acc[i >> 4][fr][i & 15];
-          if (!full && v0 + off(i) >= V) z[i] = -INFINITY;
+        for (int i = 0; i < T::FV * 16; ++i) z[i] = acc[i >> 4][fr][i & 15];
+        if (!full) {
+          // Last vocabulary tile only: entries past V drop out (the limit
+          // passes through an empty asm, so the compares stay in this
+          // uniform branch instead of running on every tile).
+          int lim = V - v0;
+          asm volatile("" : "+v"(lim));
+#pragma unroll
+          for (int i = 0; i < T::FV * 16; ++i) z[i] = off(i) >= lim ? -INFINITY : z[i];
         }
         row_fold<EXT, T::FV * 16>(run[fr], z, v0, off);
       }

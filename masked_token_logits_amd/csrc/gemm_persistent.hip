@@ -436,9 +436,17 @@ __device__ __forceinline__ void persistent_items(uint16_t* __restrict__ lds, con
               for (int fv = 0; fv < 4; ++fv) {
                 float z[16];
 #pragma unroll
-                for (int x = 0; x < 16; ++x) {
+                for (int x = 0; x < 16; ++x)
                   asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(z[x]) : "a"(acc[fv][fr][x]));
-                  if (!full && v0 + fv * 32 + off(x) >= V) z[x] = -INFINITY;
+                if (!full) {
+                  // Last vocabulary tile only: entries past V drop out.  The
+                  // limit passes through an empty asm so that neither the
+                  // compares nor the selects move out of this (uniform)
+                  // branch: there they would cost VALU on every tile.
+                  int lim = V - (v0 + fv * 32);
+                  asm volatile("" : "+v"(lim));
+#pragma unroll
+                  for (int x = 0; x < 16; ++x) z[x] = off(x) >= lim ? -INFINITY : z[x];
                 }
                 RowState r = get(fr);
                 row_fold<EXT, 16>(r, z, v0 + fv * 32, off);
@@ -855,9 +863,17 @@ __device__ __forceinline__ void persistent_items_wl(uint16_t* __restrict__ lds, 
               for (int fv = 0; fv < 4; ++fv) {
                 float z[16];
 #pragma unroll
-                for (int x = 0; x < 16; ++x) {
+                for (int x = 0; x < 16; ++x)
                   asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(z[x]) : "a"(acc[fv][fr][x]));
-                  if (!full && v0 + fv * 32 + off(x) >= V) z[x] = -INFINITY;
+                if (!full) {
+                  // Last vocabulary tile only: entries past V drop out.  The
+                  // limit passes through an empty asm so that neither the
+                  // compares nor the selects move out of this (uniform)
+                  // branch: there they would cost VALU on every tile.
+                  int lim = V - (v0 + fv * 32);
+                  asm volatile("" : "+v"(lim));
+#pragma unroll
+                  for (int x = 0; x < 16; ++x) z[x] = off(x) >= lim ? -INFINITY : z[x];
                 }
                 RowState r = get(fr);
                 row_fold<EXT, 16>(r, z, v0 + fv * 32, off);

@@ -78,19 +78,39 @@ __device__ __forceinline__ void row_merge(RowState& x, const RowState& y) {
   x.m = mn;
 }
 
+// max(a, b, c) in one v_max3_f32.  Written out because fmaxf on values the
+// compiler cannot prove quiet (accumulators read through inline asm) costs a
+// canonicalising v_max_f32 x, x, x per input first; the logits here are
+// never signalling NaNs.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // Fold N logits z[0..N-1] into the state; z[i] is vocabulary entry
 // v0 + off(i) with off increasing in i.  Entries outside the vocabulary must
-// be -inf (they then add nothing).  Strict '>' comparisons in order keep the
-// lowest index among equal maxima.
+// be -inf (they then add nothing).  The block's argmax is the lowest index
+// among equal maxima: strict '>' comparisons in order (EXT), or the maximum
+// first and then the lowest i holding it.
 template <bool EXT, int N, class Off>
 __device__ __forceinline__ void row_fold(RowState& r, const float* z, int v0, Off off) {
+  static_assert(N >= 3, "max3 tree");
   float bm = -INFINITY, b2 = -INFINITY;
   int bi = 0;
+  if constexpr (EXT) {
 #pragma unroll
-  for (int i = 0; i < N; ++i) {
-    if (EXT) b2 = __builtin_amdgcn_fmed3f(bm, b2, z[i]);  // second largest of {bm, b2, z} (bm >= b2)
-    bi = z[i] > bm ? off(i) : bi;
-    bm = fmaxf(bm, z[i]);
+    for (int i = 0; i < N; ++i) {
+      b2 = __builtin_amdgcn_fmed3f(bm, b2, z[i]);  // second largest of {bm, b2, z} (bm >= b2)
+      bi = z[i] > bm ? off(i) : bi;
+      bm = fmaxf(bm, z[i]);
+    }
+  } else {
+    bm = max3f(z[0], z[1], z[2]);
+#pragma unroll
+    for (int i = 3; i < N; i += 2) bm = max3f(bm, z[i], z[i + 1 < N ? i + 1 : i]);
+#pragma unroll
+    for (int i = N - 1; i >= 0; --i) bi = z[i] == bm ? off(i) : bi;
   }
   const float mn = fmaxf(r.m, bm);
   if (mn == -INFINITY) return;
