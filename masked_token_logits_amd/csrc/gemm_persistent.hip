@@ -676,18 +676,24 @@ __device__ __forceinline__ void persistent_items_wl(uint16_t* __restrict__ lds, 
 
     // Issue bookkeeping: stage positions are numbered from the item's first
     // stage; the hidden tile of position q goes to slot (2q) % 5 and its
-    // W_lm tile to (2q + 1) % 5.  Positions past the item's last stage re-read its last
-    // W_lm tile and hidden tile (valid memory) and are never consumed; the
-    // item's final vmcnt(0) drains them.  W_lm rows past V (last vocabulary
-    // tile only) re-read row 0 of the tile; the epilogue drops their logits.
+    // W_lm tile to (2q + 1) % 5.  Positions past the item's last stage
+    // re-read its last W_lm tile and hidden tile (valid memory) and are never
+    // consumed; the item's final vmcnt(0) drains them.  W_lm rows past V
+    // (last vocabulary tile only) re-read a chunk of row V - 1; the epilogue
+    // drops their logits.
     int wi_vt = vt_lo, wi_k0 = 0, wi_slot = 1;  // next W_lm position to issue
     int hi_k0 = 0, hi_slot = 0;                 // next hidden position to issue
     auto next_slot = [](int s) { return s + 2 >= NOP ? s + 2 - NOP : s + 2; };
     auto issue_w = [&](int j) {
       const int vbase = (wi_vt < vt_hi ? wi_vt : vt_hi - 1) * BN;
       const char* Wb = reinterpret_cast<const char*>(W + (size_t)vbase * (size_t)d + wi_k0);
-      const bool keep = vbase + BN <= V || vbase + (wave + 4 * j) * WL_ROWS + (lane >> 3) < V;
-      const uint32_t o = keep ? woff[j] : (uint32_t)((lane & 7) * 16);
+      // Rows past V (last vocabulary tile only) read the last chunk of row
+      // V - 1 instead: every valid row's offset is at most that chunk's, so
+      // one unsigned min per DMA does it (on a full tile the limit is the
+      // tile's own last chunk and changes nothing).
+      const int rows_in = min(V - vbase, BN);
+      const uint32_t wlim = (uint32_t)(((rows_in - 1) * d + (WBK - 8)) * 2);
+      const uint32_t o = min(woff[j], wlim);
       __builtin_amdgcn_global_load_lds((const void*)(Wb + o),
                                        (LDS_AS void*)(lds + wi_slot * OPT + (wave + 4 * j) * WL_ROWS * WBK), 16, 0, 0);
     };
