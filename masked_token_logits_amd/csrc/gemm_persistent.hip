@@ -14,16 +14,14 @@
 //     lane's accumulators of one 32x32 block are 16 vocabulary entries of a
 //     single row and the max / argmax / sum-exp reduction is mostly in-lane.
 //   * Operands reach LDS by direct global->LDS DMA (global_load_lds_dwordx4):
-//     no VGPR staging.  BK = 32, a 4-deep ring of (W tile, hidden tile)
-//     stages (128 KiB of the 160 KiB LDS): three stages are in flight while
-//     one is consumed.  When the readout has a single row tile (<= 256
-//     rows) the W_lm stream from HBM is the bound, and W_lm instead goes
-//     through 3 slots of stage pairs (whole 128-byte lines per row, 160 KiB
-//     in all); see persistent_items.  Waits are explicit (s_waitcnt vmcnt(N) + s_barrier)
-//     so the compiler's conservative vmcnt(0) never drains the ring.  The
-//     barrier sits between the two 16-deep K steps of a stage, so the next
-//     stage's first fragments load while the current stage's second batch
-//     of 16 MFMAs runs: LDS latency never stalls the matrix pipe.
+//     no VGPR staging.  With d % 64 == 0 (persistent_items_wl) a stage is
+//     64 deep and every DMA reads whole 128-byte lines, in a ring of five
+//     32 KiB operand slots (all 160 KiB of LDS); otherwise (d % 32 == 0,
+//     persistent_items) 32-deep stages of half lines in a 4-deep ring of
+//     (W tile, hidden tile) slots.  Waits are explicit (s_waitcnt vmcnt(N) +
+//     s_barrier) so the compiler's conservative vmcnt(0) never drains the
+//     ring, and each stage's barrier comes before its last K step, so the
+//     next stage's first fragments load while that K step's MFMAs run.
 //   * 16-byte chunks are XOR-swizzled by row so that the ds_read_b128
 //     fragment loads are bank-conflict free; the swizzle is
 //     applied by choosing each lane's global source chunk, since a DMA lane
@@ -61,15 +59,6 @@ constexpr int NT = 256;
 constexpr int TILE = BM * BK;                 // elements of one operand tile per stage
 constexpr int DMA_ROWS = 16;                  // rows written by one wave-wide DMA (64 x 16 B)
 constexpr int DMA_PER_OPERAND = BM / DMA_ROWS / 4;  // per wave per stage: 4
-// W_lm is staged in pairs of stages: NWP slots of [256 rows][64 K] (whole
-// 128-byte lines per row), filled by DMAs of 8 rows x 128 B.
-constexpr int NWP = 3;
-constexpr int WPAIR = BM * 2 * BK;                    // elements of one W_lm pair slot
-constexpr int WP_ROWS = 8;                            // rows written by one wave-wide W_lm DMA
-constexpr int W_DMA_PER_PAIR = BM / WP_ROWS / 4;      // per wave per pair: 8
-static_assert((NWP * WPAIR + NST * TILE) * 2 <= 160 * 1024, "LDS budget");
-static_assert(W_DMA_PER_PAIR + DMA_PER_OPERAND == 12 && 2 * DMA_PER_OPERAND + W_DMA_PER_PAIR == 16,
-              "the stage waits assume 12 + 4 DMAs per pair of positions");
 static_assert(BM == BN, "square tile assumed by the loader");
 static_assert(BK == 32, "swizzle and DMA layout assume 4 chunks of 16 B per row");
 
@@ -89,23 +78,17 @@ __device__ __forceinline__ float swiglu(float g, float u) {
 // MODE: kEpiReadout = online vocabulary reduction into per-slice partials
 // (rows gathered through idx, M / slices / row tiles from ctr); kEpiStore /
 // kEpiSwiGLU = bf16 output tiles (rows row 0..M-1 of H, shape from st).
-// PAIRED: which LDS ring streams W_lm.
-//   false: NST slots of (W_lm tile [256][32], hidden tile [256][32]); a W_lm
-//          DMA reads 64 bytes of each of 16 rows (half lines).
-//   true:  NWP pair slots of W_lm [256][64] (two stages' K) and NST hidden
-//          slots [256][32]; a W_lm DMA reads whole 128-byte lines of 8 rows,
-//          issued half a pair per stage.
-// Whole lines double the rate at which the W_lm stream leaves HBM when it is
-// the bound (a single row tile: 185 vs 218 us at M = 32, 267 vs 327 us at
-// M = 256 on the LLaDA-like head); with several row tiles the GEMM is MFMA
-// bound and the 4-slot ring measured 1-3% faster.
-template <int MODE, bool EXT, bool PAIRED>
+// This is the main loop for d % 64 != 0 (d % 32 == 0): NST slots of (W_lm
+// tile [256][32], hidden tile [256][32]), every DMA reading 64 bytes of each
+// of 16 rows (half lines).  It keeps 32-bit source offsets, so the host
+// takes it only while the hidden tensor spans < 4 GiB.
+template <int MODE, bool EXT>
 __device__ __forceinline__ void persistent_items(uint16_t* __restrict__ lds, const uint16_t* __restrict__ W,
                                                  const uint16_t* __restrict__ H, int d, int V,
                                                  const int32_t* __restrict__ idx,
                                                  const int32_t* __restrict__ ctr, Partials part, StoreArgs st) {
-  auto wslot = [&](int s) { return PAIRED ? lds + s * WPAIR : lds + s * 2 * TILE; };
-  auto hslot = [&](int s) { return PAIRED ? lds + NWP * WPAIR + s * TILE : lds + s * 2 * TILE + TILE; };
+  auto wslot = [&](int s) { return lds + s * 2 * TILE; };
+  auto hslot = [&](int s) { return lds + s * 2 * TILE + TILE; };
 
   const int n_vt = (V + BN - 1) / BN;
   const int M = MODE == kEpiReadout ? ctr[0] : st.M;
@@ -134,10 +117,6 @@ __device__ __forceinline__ void persistent_items(uint16_t* __restrict__ lds, con
   const int frag_row = lane & 31;
   const int frag_half = lane >> 5;
   const int frag_swz = (lane >> 2) & 3;  // f(row) for row = 32-aligned base + lane % 32
-  // W_lm pair slots hold 128 bytes per row, 8 chunks placed at chunk ^ fw(r),
-  // fw(r) = (r >> 1) & 7: the 16 rows of a ds_read_b128 phase then fill the
-  // 64 banks (even rows one half, odd rows the other, 8 distinct chunks each).
-  const int frag_swz_w = (frag_row >> 1) & 7;
 
   for (int e = xcd_remap(blockIdx.x, gridDim.x); e < n_items; e += gridDim.x) {
     int rt, slice;
@@ -171,90 +150,57 @@ __device__ __forceinline__ void persistent_items(uint16_t* __restrict__ lds, con
       const uint32_t src = MODE == kEpiReadout ? (uint32_t)idx[r] : (uint32_t)r;
       hoff[i] = (src * (uint32_t)d + (uint32_t)(dma_chunk * 8)) * 2u;
     }
-    // W_lm DMA j of this wave.  PAIRED: rows (wave + 4 j) * 8 + lane / 8,
-    // whole 128-byte lines (64 K values); the lane lands at LDS chunk
-    // lane % 8 and reads global chunk (lane % 8) ^ fw(row), fw(row) =
-    // (row >> 1) & 7.  Else rows (wave + 4 j) * 16 + lane / 4, 64 bytes, with
-    // the hidden tiles' geometry.
-    constexpr int NWD = PAIRED ? W_DMA_PER_PAIR : DMA_PER_OPERAND;
-    uint32_t woff[NWD];
+    // W_lm DMA j of this wave: rows (wave + 4 j) * 16 + lane / 4, 64 bytes,
+    // with the hidden tiles' geometry.
+    uint32_t woff[DMA_PER_OPERAND];
 #pragma unroll
-    for (int j = 0; j < NWD; ++j) {
-      if constexpr (PAIRED) {
-        const int r = (wave + 4 * j) * WP_ROWS + (lane >> 3);
-        woff[j] = (uint32_t)(r * d + (((lane & 7) ^ ((r >> 1) & 7)) * 8)) * 2u;
-      } else {
-        woff[j] = (uint32_t)(((wave + 4 * j) * DMA_ROWS + dma_row) * d + dma_chunk * 8) * 2u;
-      }
-    }
+    for (int j = 0; j < DMA_PER_OPERAND; ++j)
+      woff[j] = (uint32_t)(((wave + 4 * j) * DMA_ROWS + dma_row) * d + dma_chunk * 8) * 2u;
     const char* Hb = reinterpret_cast<const char*>(H);
 
     // Issue bookkeeping.  Stage positions are issued in order, position q
-    // = (iss_vt, iss_k0), 8 DMAs per wave: PAIRED, half of the W_lm pair of
-    // positions q - q % 2 and q - q % 2 + 1 (rows 0..127 at even q, 128..255
-    // at odd q) into pair slot iss_w and the hidden tile into hidden slot
-    // iss_h; else the W_lm and hidden tiles into ring slot iss_h.  Position
-    // q + 4 is issued during stage q, into slots stage q (and, PAIRED, the
-    // pair before it) has finished with, also past the item's last stage:
-    // those DMAs re-read the item's last W_lm tile (valid memory) and are
-    // never consumed.  The stage body is then branch-free.  Waits: stage
-    // q + 1 must have landed; the positions behind it (q + 2, q + 3) may
-    // stay in flight, 16 DMAs, except that when q + 1 starts a pair
-    // (PAIRED, q odd) the W_lm half of position q + 2 must land too: 12.
-    // The item's final vmcnt(0) drains the extra DMAs.  Rows past V (last
-    // vocabulary tile only) re-read row 0 of the tile; the epilogue drops
-    // their logits.
-    int iss_vt = vt_lo, iss_k0 = 0, iss_h = 0, iss_w = 0;
+    // = (iss_vt, iss_k0), 8 DMAs per wave: the W_lm and hidden tiles into
+    // ring slot iss_h.  Position q + 4 is issued during stage q, into the
+    // slot stage q has finished with, also past the item's last stage: those
+    // DMAs re-read the item's last W_lm tile (valid memory) and are never
+    // consumed.  The stage body is then branch-free.  Waits: stage q + 1 must
+    // have landed; the positions behind it (q + 2, q + 3) may stay in flight,
+    // 16 DMAs.  The item's final vmcnt(0) drains the extra DMAs.  Rows past V
+    // (last vocabulary tile only) re-read a chunk of row V - 1; the epilogue
+    // drops their logits.
+    int iss_vt = vt_lo, iss_k0 = 0, iss_h = 0;
     auto issue_h = [&](int j) {
       uint16_t* sb = hslot(iss_h) + (wave + 4 * j) * DMA_ROWS * BK;
       const char* Hk = Hb + (size_t)iss_k0 * 2u;
       __builtin_amdgcn_global_load_lds((const void*)(Hk + hoff[j]), (LDS_AS void*)sb, 16, 0, 0);
     };
-    // W_lm DMA j of the tile (PAIRED: pair) that starts at K offset k0 of
-    // vocabulary tile iss_vt.
-    auto issue_w = [&](int j, int k0) {
+    // W_lm DMA j of position (iss_vt, iss_k0).  Rows past V read the last
+    // chunk of row V - 1 instead: one unsigned min against a tile-uniform
+    // limit (on a full tile the tile's own last chunk, which changes nothing).
+    auto issue_w = [&](int j) {
       const int vbase = (iss_vt < vt_hi ? iss_vt : vt_hi - 1) * BN;
-      const char* Wb = reinterpret_cast<const char*>(W + (size_t)vbase * (size_t)d + k0);
-      if constexpr (PAIRED) {
-        uint16_t* sa = wslot(iss_w) + (wave + 4 * j) * WP_ROWS * (2 * BK);
-        const bool keep = vbase + BN <= V || vbase + (wave + 4 * j) * WP_ROWS + (lane >> 3) < V;
-        const uint32_t o = keep ? woff[j] : (uint32_t)((lane & 7) * 16);
-        __builtin_amdgcn_global_load_lds((const void*)(Wb + o), (LDS_AS void*)sa, 16, 0, 0);
-      } else {
-        uint16_t* sa = wslot(iss_h) + (wave + 4 * j) * DMA_ROWS * BK;
-        const bool keep = vbase + BN <= V || vbase + (wave + 4 * j) * DMA_ROWS + dma_row < V;
-        const uint32_t o = keep ? woff[j] : (uint32_t)(dma_chunk * 16);
-        __builtin_amdgcn_global_load_lds((const void*)(Wb + o), (LDS_AS void*)sa, 16, 0, 0);
-      }
+      const char* Wb = reinterpret_cast<const char*>(W + (size_t)vbase * (size_t)d + iss_k0);
+      const int rows_in = min(V - vbase, BN);
+      const uint32_t wlim = (uint32_t)(((rows_in - 1) * d + (BK - 8)) * 2);
+      uint16_t* sa = wslot(iss_h) + (wave + 4 * j) * DMA_ROWS * BK;
+      __builtin_amdgcn_global_load_lds((const void*)(Wb + min(woff[j], wlim)), (LDS_AS void*)sa, 16, 0, 0);
     };
-    // after position q (parity PAR) has been issued
-    auto advance_issue = [&](auto par_tag) {
-      constexpr int PAR = decltype(par_tag)::value;
+    auto advance_issue = [&]() {
       iss_h = (iss_h + 1) & (NST - 1);
-      if (PAIRED && PAR == 1) iss_w = iss_w + 1 == NWP ? 0 : iss_w + 1;
       iss_k0 += BK;
       if (iss_k0 == d) {
         iss_k0 = 0;
         ++iss_vt;
       }
     };
-    // W_lm DMA m (m < 4) of position q (parity PAR): PAIRED, DMA
-    // 4 PAR + m of the pair, which starts at the even position's K offset.
-    auto issue_w_pos = [&](auto par_tag, int m) {
-      constexpr int PAR = decltype(par_tag)::value;
-      if constexpr (PAIRED)
-        issue_w(PAR * (W_DMA_PER_PAIR / 2) + m, PAR == 0 ? iss_k0 : iss_k0 - BK);
-      else
-        issue_w(m, iss_k0);
-    };
-    auto issue_pos = [&](auto par_tag) {
+    auto issue_pos = [&]() {
 #pragma unroll
-      for (int m = 0; m < 4; ++m) issue_w_pos(par_tag, m);
+      for (int m = 0; m < DMA_PER_OPERAND; ++m) issue_w(m);
 #pragma unroll
       for (int j = 0; j < DMA_PER_OPERAND; ++j) issue_h(j);
-      advance_issue(par_tag);
+      advance_issue();
     };
-    static_assert(DMA_PER_OPERAND == 4 && W_DMA_PER_PAIR / 2 == 4, "4 W_lm + 4 hidden DMAs per position");
+    static_assert(DMA_PER_OPERAND == 4, "4 W_lm + 4 hidden DMAs per position");
 
     // Running state per row block, one array per field (an array of
     // RowState structs is not split into registers and lands in scratch).
@@ -286,20 +232,15 @@ __device__ __forceinline__ void persistent_items(uint16_t* __restrict__ lds, con
       run_a[fr] = r.a;
     };
 
-    // Fragment loads of K step kk (0/1) of a stage: W_lm from pair slot ws,
-    // K half `half` of the pair; hidden from slot hs.  Fragment i (i = 0..7)
-    // is W_lm block i/2 when i is even, hidden block i/2 when odd, so the
-    // first MFMA's operands arrive first.
-    auto load_frag = [&](int ws, int half, int hs, int kk, int i, bf16x8* fa, bf16x8* fb) {
+    // Fragment loads of K step kk (0/1) of a stage: W_lm from slot ws,
+    // hidden from slot hs.  Fragment i (i = 0..7) is W_lm block i/2 when i is
+    // even, hidden block i/2 when odd, so the first MFMA's operands arrive
+    // first.
+    auto load_frag = [&](int ws, int hs, int kk, int i, bf16x8* fa, bf16x8* fb) {
       const int f = i >> 1;
       if ((i & 1) == 0) {
-        if constexpr (PAIRED) {
-          const int chunk = ((half * 4 + kk * 2 + frag_half) ^ frag_swz_w) * 8;
-          fa[f] = *reinterpret_cast<const bf16x8*>(wslot(ws) + (wv * 128 + f * 32 + frag_row) * (2 * BK) + chunk);
-        } else {
-          const int chunk = ((kk * 2 + frag_half) ^ frag_swz) * 8;
-          fa[f] = *reinterpret_cast<const bf16x8*>(wslot(ws) + (wv * 128 + f * 32 + frag_row) * BK + chunk);
-        }
+        const int chunk = ((kk * 2 + frag_half) ^ frag_swz) * 8;
+        fa[f] = *reinterpret_cast<const bf16x8*>(wslot(ws) + (wv * 128 + f * 32 + frag_row) * BK + chunk);
       } else {
         const int chunk = ((kk * 2 + frag_half) ^ frag_swz) * 8;
         fb[f] = *reinterpret_cast<const bf16x8*>(hslot(hs) + ((wr + 2 * f) * 32 + frag_row) * BK + chunk);
@@ -315,20 +256,20 @@ __device__ __forceinline__ void persistent_items(uint16_t* __restrict__ lds, con
       constexpr int NFR = decltype(nfr_tag)::value;
       // Fragment i of a K step: W_lm block i/2 when i is even (needed while
       // any block is active), hidden block i/2 when odd (if that block is).
-      auto frag = [&](int ws, int half, int hs, int kk, int i, bf16x8* fa, bf16x8* fb) {
-        if ((i & 1) == 0 ? NFR > 0 : (i >> 1) < NFR) load_frag(ws, half, hs, kk, i, fa, fb);
+      auto frag = [&](int ws, int hs, int kk, int i, bf16x8* fa, bf16x8* fb) {
+        if ((i & 1) == 0 ? NFR > 0 : (i >> 1) < NFR) load_frag(ws, hs, kk, i, fa, fb);
       };
 
       // Prologue: positions 0..2 in flight, wait for position 0, queue
       // position 3, fetch stage 0's first fragments.
-      issue_pos(std::integral_constant<int, 0>{});
-      issue_pos(std::integral_constant<int, 1>{});
-      issue_pos(std::integral_constant<int, 0>{});
-      stage_sync<PAIRED ? 12 : 16>();  // position 0 (PAIRED: and the rest of pair 0, position 1's W_lm DMAs)
-      issue_pos(std::integral_constant<int, 1>{});
+      issue_pos();
+      issue_pos();
+      issue_pos();
+      stage_sync<16>();  // position 0
+      issue_pos();
       bf16x8 fxa[4], fxb[4], fya[4], fyb[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) frag(0, 0, 0, 0, i, fxa, fxb);
+      for (int i = 0; i < 8; ++i) frag(0, 0, 0, i, fxa, fxb);
 
       // One stage q: load the second K step's fragments while the first K
       // step's 16 MFMAs run; mid-stage barrier (stage q+1 landed, everyone is
@@ -342,13 +283,10 @@ __device__ __forceinline__ void persistent_items(uint16_t* __restrict__ lds, con
       // reads and force the accumulators out of AGPRs).
       f32x16 acc[4][4];
       const f32x16 zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      int cws = 0, chs = 0;  // stage q's pair slot and hidden slot
-      // PAR = q & 1: the first (0) or second (1) stage of its W_lm pair.
-      auto stage = [&](auto first_tag, auto par_tag) {
+      int cs = 0;  // stage q's ring slot
+      auto stage = [&](auto first_tag) {
         constexpr bool FIRST = decltype(first_tag)::value;
-        constexpr int PAR = decltype(par_tag)::value;
-        const int nhs = (chs + 1) & (NST - 1);  // stage q + 1's slots
-        const int nws = !PAIRED ? nhs : PAR == 0 ? cws : (cws + 1 == NWP ? 0 : cws + 1);
+        const int ns = (cs + 1) & (NST - 1);  // stage q + 1's slot
         // First K step: MFMA pair m (blocks 2m, 2m+1), then the second K
         // step's fragment m.  sched_barrier fixes the interleave.
 #pragma unroll
@@ -360,12 +298,11 @@ __device__ __forceinline__ void persistent_items(uint16_t* __restrict__ lds, con
               acc[fv][fr] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fxa[fv], fxb[fr], FIRST ? zero16 : acc[fv][fr],
                                                                     0, 0, 0);
           }
-          frag(cws, PAR, chs, 1, m, fya, fyb);
+          frag(cs, cs, 1, m, fya, fyb);
           __builtin_amdgcn_sched_barrier(0);
         }
-        // Stage q+1 landed: for odd q (q+1 starts a pair) that includes the
-        // W_lm DMAs of position q+2, so 4 + 8 DMAs may stay in flight, else 8 + 8.
-        stage_sync<(PAIRED && PAR == 1) ? 12 : 16>();
+        // Stage q+1 landed: positions q+2 and q+3 (8 + 8 DMAs) may stay in flight.
+        stage_sync<16>();
         // Second K step: MFMA pair m, position q+4's DMAs (W_lm DMA m and
         // hidden DMA m for m < 4), fragment m of stage q+1's first K step.
 #pragma unroll
@@ -376,28 +313,18 @@ __device__ __forceinline__ void persistent_items(uint16_t* __restrict__ lds, con
             if (fr < NFR) acc[fv][fr] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fya[fv], fyb[fr], acc[fv][fr], 0, 0, 0);
           }
           if (m < 4)
-            issue_w_pos(par_tag, m);
+            issue_w(m);
           else
             issue_h(m - 4);
-          frag(nws, PAR ^ 1, nhs, 0, m, fxa, fxb);
+          frag(ns, ns, 0, m, fxa, fxb);
           __builtin_amdgcn_sched_barrier(0);
         }
-        advance_issue(par_tag);
-        cws = nws;
-        chs = nhs;
+        advance_issue();
+        cs = ns;
       };
       for (int vt = vt_lo; vt < vt_hi; ++vt) {
-        if constexpr (PAIRED) {  // stage parity decides the W_lm pair bookkeeping: unrolled by two
-          stage(std::true_type{}, std::integral_constant<int, 0>{});
-          stage(std::false_type{}, std::integral_constant<int, 1>{});
-          for (int ks = 2; ks < KT; ks += 2) {
-            stage(std::false_type{}, std::integral_constant<int, 0>{});
-            stage(std::false_type{}, std::integral_constant<int, 1>{});
-          }
-        } else {
-          stage(std::true_type{}, std::integral_constant<int, 0>{});
-          for (int ks = 1; ks < KT; ++ks) stage(std::false_type{}, std::integral_constant<int, 0>{});
-        }
+        stage(std::true_type{});
+        for (int ks = 1; ks < KT; ++ks) stage(std::false_type{});
         if constexpr (NFR > 0) {
           // Online reduction of the finished vocabulary tile, one 16-value
           // block at a time.  Accumulator x of block (fv, fr) is vocabulary
@@ -1026,13 +953,13 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_persistent(const uint16_t* __res
                                                           StoreArgs st) {
   // One array for both layouts (separate arrays make the compiler drain
   // vmcnt at every fragment read).
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[NWP * WPAIR + NST * TILE];
-  static_assert(NST * 2 * TILE <= NWP * WPAIR + NST * TILE, "LDS layouts");
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[NOP * OPT];
+  static_assert(NST * 2 * TILE <= NOP * OPT, "LDS layouts");
   if ((d & (WBK - 1)) == 0) {
     persistent_items_wl<MODE, EXT>(lds, W, H, d, V, idx, ctr, part, st);
     return;
   }
-  persistent_items<MODE, EXT, false>(lds, W, H, d, V, idx, ctr, part, st);
+  persistent_items<MODE, EXT>(lds, W, H, d, V, idx, ctr, part, st);
 }
 
 }  // namespace
