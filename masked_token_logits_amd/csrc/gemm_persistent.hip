@@ -522,17 +522,18 @@ __device__ __forceinline__ void persistent_items(uint16_t* __restrict__ lds, con
 //
 // Stage q, four 16-deep K steps of 16 MFMAs per wave, each K step's MFMAs
 // interleaved with the next K step's fragment loads:
-//   K step 0:    also the DMAs of hidden tile q + 2 (into the slot W_lm tile
-//                q - 1 held);
+//   K steps 0-1: also the DMAs of hidden tile q + 2 (into the slot W_lm tile
+//                q - 1 held), after every other MFMA pair (one DMA per pair,
+//                all in K step 0, measured 1-2% slower);
 //   barrier B(q) after K step 2: this wave's reads of stage q are done
 //                (lgkmcnt(0)) and stage q + 1 has landed (vmcnt(8): only
 //                hidden tile q + 2 may be in flight);
 //   K step 3:    also the DMAs of W_lm tile q + 2 (into the slot hidden tile
 //                q held) and stage q + 1's first fragments.
 // So hidden tiles are queued about two stages before use and W_lm tiles one
-// (the gathered hidden rows miss L2 more often: each XCD's L2 holds four
-// W_lm tiles per hidden tile in flight, and W_lm tiles are shared by all
-// XCDs in the Infinity Cache), and a wave meets one barrier per 64 MFMAs.
+// (five slots allow no more; the other way round measured 7.5% slower on the
+// 128k-position high-mask step, whose gathered hidden tiles stream from the
+// Infinity Cache), and a wave meets one barrier per 64 MFMAs.
 // The prologue queues the hidden and W_lm tiles of stages 0 and 1.
 constexpr int WBK = kPersistWideBK;            // K per stage
 constexpr int OPT = BM * WBK;                  // elements of one operand tile [256][64]
@@ -738,11 +739,14 @@ __device__ __forceinline__ void persistent_items_wl(uint16_t* __restrict__ lds, 
       auto stage = [&](auto first_tag) {
         const int nws = next_slot(cws), nhs = next_slot(chs);  // stage q + 1's slots
         kstep(fxa, fxb, first_tag, [&](int m) {
-          issue_h(m);
+          if ((m & 1) == 0) issue_h(m >> 1);
           frag(cws, chs, 1, m, fya, fyb);
         });
+        kstep(fya, fyb, std::false_type{}, [&](int m) {
+          if ((m & 1) == 0) issue_h(4 + (m >> 1));
+          frag(cws, chs, 2, m, fxa, fxb);
+        });
         advance_h();
-        kstep(fya, fyb, std::false_type{}, [&](int m) { frag(cws, chs, 2, m, fxa, fxb); });
         kstep(fxa, fxb, std::false_type{}, [&](int m) { frag(cws, chs, 3, m, fya, fyb); });
         // B(q): stage q + 1 landed (only the hidden tile of q + 2 may be in
         // flight) and every wave is done reading stage q.
