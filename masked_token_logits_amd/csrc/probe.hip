@@ -9,7 +9,9 @@
 //   mode 1: per 64-deep stage and wave, 64 MFMAs, 32 ds_read_b128 fragment
 //           loads and 16 whole-line global_load_lds DMAs (8 rows x 128 B)
 //           from an L2-resident 4 MiB region of `src` per XCD, one barrier
-//           with vmcnt(8): the main loop's schedule and LDS layout.
+//           with vmcnt(8): the main loop's schedule (8 DMAs after every
+//           other MFMA pair of K steps 0 and 1, 8 after every pair of K
+//           step 3) and LDS layout.
 // One 256-thread workgroup per compute unit, one wave per SIMD, as the GEMM.
 #include "dllm_probe.h"
 
@@ -70,7 +72,9 @@ __global__ __launch_bounds__(256, 1) void k_probe(const uint16_t* __restrict__ s
     __builtin_amdgcn_global_load_lds((const void*)p, (LDS_AS void*)(lds + slot * kSlotElems + (wave + 4 * j) * 512),
                                      16, 0, 0);
   };
-  auto kstep = [&](int cur, int kk, bool issue) {
+  // issue: 0 no DMAs, 1 one after every MFMA pair, 2 / 3 DMAs 0-3 / 4-7
+  // after every other pair
+  auto kstep = [&](int cur, int kk, int issue) {
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
 #pragma unroll
@@ -79,7 +83,8 @@ __global__ __launch_bounds__(256, 1) void k_probe(const uint16_t* __restrict__ s
         acc[fv][fr] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][fv], fb[cur][fr], acc[fv][fr], 0, 0, 0);
       }
       if (MODE == 1) {
-        if (issue) dma(m);
+        if (issue == 1) dma(m);
+        if (issue >= 2 && (m & 1) == 0) dma((issue - 2) * 4 + (m >> 1));
         frag(kk, m, fa[cur ^ 1], fb[cur ^ 1]);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -99,16 +104,16 @@ __global__ __launch_bounds__(256, 1) void k_probe(const uint16_t* __restrict__ s
     w0 = wall_clock64();
   }
   for (int q = 0; q < stages; ++q) {
-    kstep(0, 1, true);
-    kstep(1, 2, false);
-    kstep(0, 3, false);
+    kstep(0, 1, 2);
+    kstep(1, 2, 3);
+    kstep(0, 3, 0);
     if (MODE == 1) {
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_waitcnt((8 & 15) | (7 << 4) | (0 << 8));
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
     }
-    kstep(1, 0, true);
+    kstep(1, 0, 1);
     k0 = (k0 + 64) & 4095;
     slot = slot == kSlots - 1 ? 0 : slot + 1;
   }
