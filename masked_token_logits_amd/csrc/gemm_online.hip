@@ -229,7 +229,7 @@ __global__ __launch_bounds__(T::NT, T::MIN_WAVES) void k_gemm_online(const uint1
       // (fv, fr) in this lane is vocabulary entry
       //   v0 + fv*32 + 8*(e/4) + 4*(lane/32) + e%4
       // of row wr*WR + fr*32 + lane%32; for a fixed lane these increase
-      // with (fv, e), so a strict '>' scan keeps the lowest index.
+      // with (fv, e), the order row_fold needs to keep the lowest index.
       const int v0 = vt * T::BN + wv * T::WV + 4 * frag_half;
       const bool full = (vt + 1) * T::BN <= V;
       auto off = [](int i) { return (i >> 4) * 32 + 8 * ((i & 15) >> 2) + (i & 3); };

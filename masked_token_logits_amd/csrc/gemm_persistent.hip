@@ -330,8 +330,8 @@ __device__ __forceinline__ void persistent_items(uint16_t* __restrict__ lds, con
           // block at a time.  Accumulator x of block (fv, fr) is vocabulary
           // entry v0 + fv*32 + 8*(x/4) + x%4 of local row (wr + 2 fr)*32 + lane%32,
           // with v0 = tile base + wv*128 + 4*(lane/32).  Within a lane the
-          // index grows with (fv, x); strict '>' comparisons in that order
-          // keep the lowest index among equal maxima.
+          // index grows with (fv, x), the order row_fold needs to keep the
+          // lowest index among equal maxima.
           // The accumulators are read with explicit v_accvgpr_read (inline
           // asm): left to itself the register allocator copies all 256 of
           // them to VGPRs at once and spills.  The compiler does not see these
@@ -767,8 +767,8 @@ __device__ __forceinline__ void persistent_items_wl(uint16_t* __restrict__ lds, 
           // block at a time.  Accumulator x of block (fv, fr) is vocabulary
           // entry v0 + fv*32 + 8*(x/4) + x%4 of local row (wr + 2 fr)*32 + lane%32,
           // with v0 = tile base + wv*128 + 4*(lane/32).  Within a lane the
-          // index grows with (fv, x); strict '>' comparisons in that order
-          // keep the lowest index among equal maxima.
+          // index grows with (fv, x), the order row_fold needs to keep the
+          // lowest index among equal maxima.
           // The accumulators are read with explicit v_accvgpr_read (inline
           // asm): left to itself the register allocator copies all 256 of
           // them to VGPRs at once and spills.  The compiler does not see these
